@@ -1,0 +1,292 @@
+"""Benchmark of the MXFP4 MoE expert path on one MI355X.
+
+A step is one pass of the whole path over one batch: activation quantisation,
+routing + permutation, the grouped FC1 (+ fused SwiGLU / requantisation) and
+FC2 GEMMs, and the gate-weighted combine - all on device-resident inputs.
+
+Headline workload: the 16384-token prefill layer with FP4 x FP4 products
+(hidden 7168, intermediate 2048, 256 experts, top-6, MXFP4 activations),
+value = algorithmic TFLOP/s of the layer (pairs x 88,080,384 flop / step time).
+Also reported on the same line: the 8-token decode layer (weight GB/s over the
+touched experts) and the dense 64 x 4096 x 7168 GEMM, each against its roofline.
+The fp64 CPU oracle is timed on a bounded sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|decode|dense]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from mxfp4_block_scaled_amd import datagen as dg  # noqa: E402
+from mxfp4_block_scaled_amd import ops  # noqa: E402
+
+METRIC = "MoE MXFP4 grouped-GEMM TFLOP/s (prefill) & weight GB/s (decode) vs roofline"
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"e2m1": 10100.0, "e4m3": 5000.0}  # dense MXFP4 / MXFP8 (FP8 x FP4 runs at the FP8 rate)
+FLOP_PER_PAIR = 2 * 7168 * 4096 + 2 * 2048 * 7168  # 88,080,384
+BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,352
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def moe_weights_dev(cfg):
+    """All experts' weights, generated expert by expert straight into device tensors."""
+    E, H, I = cfg["E"], cfg["H"], cfg["I"]
+    w1 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device="cuda")
+    s1 = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device="cuda")
+    w2 = torch.empty((E, H, I // 2), dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((E, H, I // 32), dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        parts = dg.expert_weights(cfg["seed"], e, H, I, cfg["exp_lo"], cfg["exp_hi"])
+        for dst, src in zip((w1, s1, w2, s2), parts):
+            dst[e].copy_(torch.from_numpy(src), non_blocking=False)
+    return w1, s1, w2, s2
+
+
+class Layer:
+    """Pre-allocated buffers of one MoE layer; step() = the four C-ABI calls."""
+
+    def __init__(self, cfg, weights_sets, y_dtype=torch.bfloat16):
+        self.cfg = cfg
+        T, H, I, k = cfg["T"], cfg["H"], cfg["I"], cfg["k"]
+        self.fmt = cfg["act_fmt"]
+        self.x = bf16_dev(dg.activations(cfg["seed"], T, H))
+        self.logits = to_dev(dg.logits(cfg["seed"], T, cfg["E"], cfg["routing"]))
+        self.sets = weights_sets
+        self.y_dtype = y_dtype
+        self.T, self.k = T, k
+        R = T * k
+        fp4 = self.fmt == "e2m1"
+        self.q = torch.empty((T, H // 2 if fp4 else H), dtype=torch.uint8, device="cuda")
+        self.qs = torch.empty((T, H // 32), dtype=torch.uint8, device="cuda")
+        self.ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        self.gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        self.offs = torch.empty((cfg["E"] + 1,), dtype=torch.int32, device="cuda")
+        self.sp = torch.empty((R,), dtype=torch.int32, device="cuda")
+        self.pr = torch.empty((R,), dtype=torch.int32, device="cuda")
+        self.h = torch.empty((R, I // 2 if fp4 else I), dtype=torch.uint8, device="cuda")
+        self.hs = torch.empty((R, I // 32), dtype=torch.uint8, device="cuda")
+        self.y = torch.empty((R, H), dtype=y_dtype, device="cuda")
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        self.lib = ops.load()
+        self.i = 0
+
+    def step(self, ev=None):
+        c, lib = self.cfg, self.lib
+        st = ctypes_stream()
+        P = ops._ptr
+        w1, s1, w2, s2 = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        f = ops.FMTS[self.fmt]
+        if ev: ev[0].record()
+        ops._check(lib.mxfp4_quantize_act(P(self.x), ops.MXF_BF16, self.T, c["H"], f, P(self.q), P(self.qs), st),
+                   "quantize")
+        if ev: ev[1].record()
+        ops._check(lib.moe_route_permute(P(self.logits), self.T, c["E"], self.k, P(self.ids), P(self.gates),
+                                         P(self.offs), P(self.sp), P(self.pr), st), "route")
+        if ev: ev[2].record()
+        ops._check(lib.moe_grouped_mxfp4_gemm(P(self.q), P(self.qs), f, self.T, self.k, c["H"], c["I"], c["E"],
+                                              P(self.offs), P(self.sp), P(w1), P(s1), P(w2), P(s2), P(self.h),
+                                              P(self.hs), P(self.y), ops.DTYPES[self.y_dtype], st), "grouped")
+        if ev: ev[3].record()
+        ops._check(lib.moe_unpermute_combine(P(self.y), ops.DTYPES[self.y_dtype], P(self.gates), P(self.pr),
+                                             self.T, self.k, c["H"], P(self.out), ops.MXF_BF16, st), "combine")
+        if ev: ev[4].record()
+
+
+def ctypes_stream():
+    import ctypes
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def time_steps(step_fn, steps, warmup, nev=0):
+    for _ in range(warmup):
+        step_fn(None)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)] if nev else None
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step_fn(evs[i] if evs else None)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    stages = None
+    if evs:
+        stages = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(nev - 1)] for i in range(steps)])
+    return wall, stages
+
+
+def bench_moe(name, steps, warmup, rotate):
+    cfg = dg.WORKLOADS[name]
+    log(f"[bench] {name}: generating inputs ...")
+    t0 = time.time()
+    base = moe_weights_dev(cfg)
+    sets = [base] + [tuple(t.clone() for t in base) for _ in range(rotate - 1)]
+    layer = Layer(cfg, sets)
+    log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s ({rotate} weight set(s))")
+    wall, st = time_steps(layer.step, steps, warmup, nev=5)
+    names = ["quantize", "route_permute", "grouped_gemm", "combine"]
+    stage_ms = {n: float(np.mean(st[:, j])) for j, n in enumerate(names)}
+    offs = layer.offs.cpu().numpy()
+    counts = np.diff(offs)
+    touched = int((counts > 0).sum())
+    pairs = cfg["T"] * cfg["k"]
+    flops = pairs * FLOP_PER_PAIR
+    wbytes = touched * BYTES_PER_EXPERT
+    return dict(cfg=cfg, ms=wall * 1e3, stage_ms=stage_ms, touched=touched, pairs=pairs, flops=flops,
+                wbytes=wbytes, max_rows=int(counts.max()), layer=layer)
+
+
+def bench_dense(steps, warmup, rotate=48):
+    cfg = dg.WORKLOADS["dense_m64_n4096_k7168"]
+    d = dg.workload_inputs("dense_m64_n4096_k7168")
+    a = bf16_dev(d["a"])
+    w0, s0 = to_dev(d["w"]), to_dev(d["w_scale"])
+    sets = [(w0, s0)] + [(w0.clone(), s0.clone()) for _ in range(rotate - 1)]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    lib = ops.load()
+    ws = torch.empty(lib.mxfp4_gemm_workspace_bytes(M, K, 0), dtype=torch.uint8, device="cuda")
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    it = [0]
+
+    def step(ev):
+        w, s = sets[it[0] % len(sets)]
+        it[0] += 1
+        if ev: ev[0].record()
+        ops._check(lib.mxfp4_gemm(ops._ptr(a), M, N, K, 0, ops._ptr(w), ops._ptr(s), ops._ptr(c), ops._ptr(ws),
+                                  ws.numel(), ctypes_stream()), "mxfp4_gemm")
+        if ev: ev[1].record()
+
+    wall, st = time_steps(step, steps * 10, warmup, nev=2)
+    ms = float(np.mean(st[:, 0]))
+    wbytes = N * K // 2 + N * K // 32
+    return dict(ms=ms, wbytes=wbytes, gbs=wbytes / (ms * 1e-3) / 1e9, flops=2 * M * N * K)
+
+
+def cpu_baseline(name, budget_s=15.0):
+    """The fp64 oracle (as it stands) on a bounded sample: whole experts of the
+    headline layer, all their rows, until ~budget_s of CPU time is spent."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    cfg = dg.WORKLOADS[name]
+    T, H, I, k, E = cfg["T"], cfg["H"], cfg["I"], cfg["k"], cfg["E"]
+    x = dg.activations(cfg["seed"], T, H)
+    logits = dg.logits(cfg["seed"], T, E, cfg["routing"])
+    fmt = cfg["act_fmt"]
+    t0 = time.perf_counter()
+    q, qs = oracle.moe.quantize_act(oracle.bf16_bits_to_f64(x), fmt)
+    ids, gates = oracle.route_topk(logits, k)
+    offs, sp, pr = oracle.permute(ids, E)
+    t_pre = time.perf_counter() - t0
+    done_pairs, t_gemm, e = 0, 0.0, 0
+    while e < E and (t_gemm < budget_s or e == 0):
+        w1, s1, w2, s2 = dg.expert_weights(cfg["seed"], e, H, I, cfg["exp_lo"], cfg["exp_hi"])
+        rows = np.arange(offs[e], offs[e + 1])
+        t1 = time.perf_counter()
+        tok = sp[rows] // k
+        a_hat = oracle.moe.decode_act(q[tok], qs[tok], fmt)
+        G, hp = oracle.fc1_swiglu_rows(a_hat, w1, s1, I)
+        hq, hs = oracle.moe.quantize_act(hp, fmt)
+        oracle.fc2_rows(hq, hs, fmt, w2, s2)
+        t_gemm += time.perf_counter() - t1
+        done_pairs += rows.size
+        e += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    tflops = done_pairs * FLOP_PER_PAIR / t_gemm / 1e12
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{name}: quantize+route+permute of all {T} tokens ({t_pre:.1f}s), then FC1+SwiGLU+"
+                      f"requantise+FC2 in fp64 for experts 0..{e - 1} ({done_pairs} pairs, {t_gemm:.1f}s); "
+                      f"value = sampled pairs x 88,080,384 flop / FC time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "dense"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the expert path here is the "
+              "single-GPU kernel; no multi-GPU figure is measured.", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ops.load()
+    torch.cuda.synchronize()
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+
+    if args.only in (None, "prefill"):
+        name = "moe_prefill_t16384_fp4"
+        r = bench_moe(name, args.steps, args.warmup, rotate=1)
+        cfg = r["cfg"]
+        tflops = r["flops"] / (r["ms"] * 1e-3) / 1e12
+        g_ms = r["stage_ms"]["grouped_gemm"]
+        g_tflops = r["flops"] / (g_ms * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[cfg["act_fmt"]]
+        result.update({
+            "value": round(tflops, 3), "unit": "TFLOP/s", "ms_per_step": round(r["ms"], 4),
+            "dtype": "mxfp4 (e2m1 x e2m1, ue8m0 scales, fp32 accumulate)",
+            "config": {"workload": name, "T": cfg["T"], "H": cfg["H"], "I": cfg["I"], "E": cfg["E"],
+                       "topk": cfg["k"], "act_fmt": cfg["act_fmt"], "routing": cfg["routing"],
+                       "seed": cfg["seed"], "pairs": r["pairs"], "max_rows_per_expert": r["max_rows"]},
+            "stages_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
+            "roofline": {"kernel": "moe_grouped_mxfp4_gemm (FC1 + FC2 kernels)", "bound": "mfma",
+                         "achieved": round(g_tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                         "frac": round(g_tflops / peak, 4), "traffic": None},
+        })
+        del r["layer"]
+        torch.cuda.empty_cache()
+    if args.only in (None, "decode"):
+        name = "moe_decode_t8"
+        r = bench_moe(name, args.steps * 5, args.warmup, rotate=2)
+        g_ms = r["stage_ms"]["grouped_gemm"]
+        dec = {"workload": name, "ms_per_step": round(r["ms"], 4),
+               "stages_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
+               "touched_experts": r["touched"], "weight_bytes": r["wbytes"],
+               "weight_GBps_layer": round(r["wbytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+               "weight_GBps_grouped_gemm": round(r["wbytes"] / (g_ms * 1e-3) / 1e9, 1),
+               "roofline": {"kernel": "moe_grouped_mxfp4_gemm (FC1 + FC2 kernels)", "bound": "hbm",
+                            "achieved": round(r["wbytes"] / (g_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(r["wbytes"] / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                            "traffic": None}}
+        if "value" not in result:
+            result.update({"value": dec["weight_GBps_layer"], "unit": "GB/s", "ms_per_step": dec["ms_per_step"],
+                           "dtype": "mxfp8 x mxfp4 (e4m3 x e2m1, fp32 accumulate)",
+                           "config": {"workload": name}, "roofline": dec["roofline"]})
+        result["decode"] = dec
+        del r["layer"]
+        torch.cuda.empty_cache()
+    if args.only in (None, "dense"):
+        r = bench_dense(args.steps, args.warmup)
+        result["dense"] = {"workload": "dense_m64_n4096_k7168", "ms": round(r["ms"], 5),
+                           "weight_GBps": round(r["gbs"], 1), "frac_hbm": round(r["gbs"] / PEAK_HBM_GBS, 4),
+                           "TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2)}
+    if not args.no_cpu and args.only in (None, "prefill"):
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline("moe_prefill_t16384_fp4")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

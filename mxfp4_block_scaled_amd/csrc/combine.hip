@@ -1,0 +1,78 @@
+// Gate-weighted unpermute-combine (the "combine" half of MoE dispatch/combine,
+// page "Domestic GPUs are awesome! Moore thread full-link adaptation DeepSeek-V4"):
+//   out[t][n] = sum_{j=0..topk-1} gates[t][j] * y[pair_row[t*topk+j]][n]
+// fp32 fused multiply-add in slot order j = 0..topk-1, then bf16 (RNE) or fp32.
+// One thread owns 8 consecutive columns of one token: 16 B (bf16) / 32 B (fp32)
+// per y row read, 16 B / 32 B written. HBM-bound.
+#include "launch.hpp"
+
+namespace mxf {
+
+template <bool kYBF16>
+__device__ __forceinline__ void load8(const void* y, int64_t off, float (&v)[8]) {
+  if (kYBF16) {
+    uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + off);
+    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(ws[j] << 16);
+      v[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(y) + off);
+    float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <bool kYBF16, bool kOutBF16>
+__global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ y,
+                                                      const float* __restrict__ gates,
+                                                      const int32_t* __restrict__ pair_row,
+                                                      int64_t T, int topk, int64_t H,
+                                                      void* __restrict__ out) {
+  const int64_t per_row = H / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= T * per_row) return;
+  const int64_t t = idx / per_row;
+  const int64_t col = (idx - t * per_row) * 8;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int j = 0; j < topk; ++j) {
+    const float g = gates[t * topk + j];
+    const int64_t r = pair_row[t * topk + j];
+    float v[8];
+    load8<kYBF16>(y, r * H + col, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+  }
+  if (kOutBF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = bf16_round(acc[2 * i]) | (bf16_round(acc[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + t * H + col) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + t * H + col);
+    p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
+int launch_combine(const void* y, bool y_bf16, const float* gates, const int32_t* pair_row,
+                   int64_t T, int topk, int64_t H, void* out, bool out_bf16, hipStream_t stream) {
+  const int64_t n = T * (H / 8);
+  if (n == 0) return 0;
+  dim3 grid((unsigned)cdiv(n, 256)), block(256);
+  if (y_bf16) {
+    if (out_bf16) combine_kernel<true, true><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
+    else combine_kernel<true, false><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
+  } else {
+    if (out_bf16) combine_kernel<false, true><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
+    else combine_kernel<false, false><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace mxf

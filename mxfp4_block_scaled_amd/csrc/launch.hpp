@@ -1,0 +1,35 @@
+// Internal launchers (host side). Each returns 0 on success, -1 if a launch failed.
+// Arguments are validated by the C ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace mxf {
+
+int launch_quantize_act(const void* x, bool f32_in, int64_t rows, int64_t K, bool fp4, uint8_t* q,
+                        uint8_t* q_scale, hipStream_t stream);
+
+// routing: returns 1 if the sizes are outside what the kernels handle (nothing launched)
+int route_permute_supported(int64_t T, int E, int topk);
+int launch_route_permute(const float* logits, int64_t T, int E, int topk, int32_t* topk_ids,
+                         float* gates, int32_t* expert_offsets, int32_t* sorted_pair,
+                         int32_t* pair_row, hipStream_t stream);
+
+int launch_combine(const void* y, bool y_bf16, const float* gates, const int32_t* pair_row,
+                   int64_t T, int topk, int64_t H, void* out, bool out_bf16, hipStream_t stream);
+
+// dense C[M][N] (fp32) = A_hat (already quantised, [M][K] codes + scales) x W_hat^T
+int launch_dense_gemm(const uint8_t* qa, const uint8_t* qa_scale, bool act_fp4, int64_t M, int64_t N,
+                      int64_t K, const uint8_t* w, const uint8_t* w_scale, float* c,
+                      hipStream_t stream);
+
+int launch_grouped_gemm(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, int64_t T, int topk,
+                        int64_t H, int64_t I, int E, const int32_t* expert_offsets,
+                        const int32_t* sorted_pair, const uint8_t* w1, const uint8_t* w1_scale,
+                        const uint8_t* w2, const uint8_t* w2_scale, uint8_t* h, uint8_t* h_scale,
+                        void* y, bool y_bf16, hipStream_t stream);
+
+}  // namespace mxf

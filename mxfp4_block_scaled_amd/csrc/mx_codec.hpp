@@ -1,0 +1,95 @@
+// Bit-exact MX block quantisation on the device (integer arithmetic on fp32 bits).
+//
+// One 32-element block follows the OCP Microscaling (MX) v1.0 conversion with
+// the element formats the pages name: E2M1 (1 sign / 2 exponent / 1 mantissa
+// bit, page "DGX Spark 原生 FP4 矩阵指令" section 一, with the UE8M0 block scale
+// of the same section) and E4M3 (4 exponent / 3 mantissa bits, page
+// "企业官网建设流程全解析" section 一, OCP "FN" variant: no infinities, max 448).
+//   scale byte  = max(0, biased exponent of amax - emax)   (emax 8 / 2)
+//               = clamp(floor(log2 amax) - emax + 127, 0, 254) for finite amax
+//   element     = round-to-nearest-even of v * 2^(127 - byte) on the element
+//                 grid (subnormals included), saturating at the largest normal,
+//                 sign bit copied from v (so -0 and negative underflow give -0).
+// The multiply by a power of two is exact unless the product falls below
+// 2^-126, where every element code is 0 anyway.
+#pragma once
+
+#include "common.hpp"
+
+namespace mxf {
+
+constexpr uint32_t kEmaxE4M3 = 8;
+constexpr uint32_t kEmaxE2M1 = 2;
+
+__device__ __forceinline__ uint32_t scale_byte_from_amax_bits(uint32_t amax_bits, uint32_t emax) {
+  uint32_t e = (amax_bits >> 23) & 0xFFu;
+  return e > emax ? e - emax : 0u;
+}
+
+// 2^(127 - byte) as fp32; valid for byte in [0, 253] (the quantiser produces <= 246)
+__device__ __forceinline__ float inv_scale_from_byte(uint32_t byte) {
+  return __uint_as_float((254u - byte) << 23);
+}
+
+// |t| -> 7-bit E4M3 magnitude code (0x00 .. 0x7E)
+__device__ __forceinline__ uint32_t e4m3_mag_code(float a) {
+  if (a >= 448.0f) return 0x7Eu;
+  if (a < 0.015625f) {  // below 2^-6: subnormal grid m * 2^-9, m = 0..8 (8 = 2^-6)
+    return (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  uint32_t u = __float_as_uint(a);
+  uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;  // (exp << 3 | m3), rounded
+  return r - ((127u - 7u) << 3);
+}
+
+// |t| -> 3-bit E2M1 magnitude code (0 .. 7)
+__device__ __forceinline__ uint32_t e2m1_mag_code(float a) {
+  if (a >= 6.0f) return 7u;
+  if (a < 1.0f) return (uint32_t)__builtin_rintf(a * 2.0f);  // 0, 0.5, 1.0
+  uint32_t u = __float_as_uint(a);
+  uint32_t r = (u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22;  // (exp << 1 | m1), rounded
+  uint32_t c = r - ((127u - 1u) << 1);
+  return c > 7u ? 7u : c;
+}
+
+__device__ __forceinline__ uint32_t e4m3_code(float v, float inv_scale) {
+  uint32_t s = (__float_as_uint(v) >> 24) & 0x80u;
+  return s | e4m3_mag_code(fabsf(v) * inv_scale);
+}
+
+__device__ __forceinline__ uint32_t e2m1_code(float v, float inv_scale) {
+  uint32_t s = (__float_as_uint(v) >> 28) & 0x8u;
+  return s | e2m1_mag_code(fabsf(v) * inv_scale);
+}
+
+// Quantise 32 fp32 values of one block held by one thread.
+// E4M3: out32 receives 32 bytes (8 words, little-endian element order).
+// E2M1: out32 receives 16 bytes (4 words), element 2n in the low nibble of byte n.
+template <bool kFP4>
+__device__ __forceinline__ uint32_t quantize_block32(const float (&v)[32], uint32_t (&out)[8]) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  const uint32_t byte = scale_byte_from_amax_bits(amax, kFP4 ? kEmaxE2M1 : kEmaxE4M3);
+  const float inv = inv_scale_from_byte(byte);
+  if (kFP4) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) word |= e2m1_code(v[w * 8 + n], inv) << (4 * n);
+      out[w] = word;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) word |= e4m3_code(v[w * 4 + n], inv) << (8 * n);
+      out[w] = word;
+    }
+  }
+  return byte;
+}
+
+}  // namespace mxf

@@ -75,7 +75,7 @@ def logits(seed, T, E, routing="normal"):
 
 def _random_bytes(g, shape):
     n = int(np.prod(shape))
-    return np.frombuffer(g.bytes(n), dtype=np.uint8).reshape(shape)
+    return np.frombuffer(bytearray(g.bytes(n)), dtype=np.uint8).reshape(shape)
 
 
 def _scale_bytes(g, shape, lo, hi):

@@ -1,0 +1,118 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects bad arguments with the documented status before any HIP
+call (so these run without a GPU; no compute call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mxfp4_block_scaled_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4_moe.h")
+
+OK, NULL, SHAPE, ALIGN, FORMAT, UNSUPPORTED, LAUNCH, WORKSPACE = range(8)
+P = ctypes.c_void_p
+
+
+def _lib():
+    if not os.path.exists(ops.lib_path()):
+        pytest.skip("library not built (run __graft_entry__.build())")
+    return ops.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_five_entry_points():
+    names = set(_declared())
+    for n in ["mxfp4_quantize_act", "mxfp4_gemm", "moe_route_permute", "moe_grouped_mxfp4_gemm",
+              "moe_unpermute_combine"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.mxf_abi_version() == 1
+    for s in range(8):
+        assert lib.mxf_status_str(s)
+
+
+A = P(4096)      # a fake, aligned, non-null device address (never dereferenced: validation fails first)
+U = P(4096 + 4)  # misaligned
+
+
+def test_quantize_errors():
+    lib = _lib()
+    assert lib.mxfp4_quantize_act(A, 1, 4, 48, 0, A, A, None) == SHAPE        # K % 32
+    assert lib.mxfp4_quantize_act(A, 1, -1, 64, 0, A, A, None) == SHAPE
+    assert lib.mxfp4_quantize_act(A, 7, 4, 64, 0, A, A, None) == FORMAT       # dtype
+    assert lib.mxfp4_quantize_act(A, 1, 4, 64, 3, A, A, None) == FORMAT       # element format
+    assert lib.mxfp4_quantize_act(None, 1, 4, 64, 0, A, A, None) == NULL
+    assert lib.mxfp4_quantize_act(U, 1, 4, 64, 0, A, A, None) == ALIGN
+    assert lib.mxfp4_quantize_act(None, 1, 0, 64, 0, None, None, None) == OK  # empty: nothing to do
+
+
+def test_gemm_errors():
+    lib = _lib()
+    need = lib.mxfp4_gemm_workspace_bytes(16, 4096, 0)
+    assert need >= 16 * 4096 + 16 * 128
+    assert lib.mxfp4_gemm_workspace_bytes(16, 4096, 1) < need
+    assert lib.mxfp4_gemm(A, 16, 32, 4096 + 64, 0, A, A, A, A, need, None) == SHAPE  # K % 512
+    assert lib.mxfp4_gemm(A, 16, 40, 4096, 0, A, A, A, A, need, None) == SHAPE       # N % 16
+    assert lib.mxfp4_gemm(A, 16, 32, 4096, 2, A, A, A, A, need, None) == FORMAT
+    assert lib.mxfp4_gemm(A, 16, 32, 4096, 0, None, A, A, A, need, None) == NULL
+    assert lib.mxfp4_gemm(A, 16, 32, 4096, 0, A, A, A, A, need - 1, None) == WORKSPACE
+    assert lib.mxfp4_gemm(A, 16, 32, 4096, 0, A, A, A, None, need, None) == WORKSPACE
+    assert lib.mxfp4_gemm(A, 16, 32, 4096, 0, A, U, A, A, need, None) == ALIGN
+    assert lib.mxfp4_gemm(None, 0, 32, 4096, 0, None, None, None, None, 0, None) == OK
+
+
+def test_route_errors():
+    lib = _lib()
+    args = [A, A, A, A, A, None]
+    assert lib.moe_route_permute(A, 8, 256, 9, *args) == SHAPE         # topk > 8
+    assert lib.moe_route_permute(A, 8, 4, 6, *args) == SHAPE           # topk > E
+    assert lib.moe_route_permute(A, 8, 256, 0, *args) == SHAPE
+    assert lib.moe_route_permute(A, 8, 2048, 6, *args) == UNSUPPORTED  # E > 1024
+    assert lib.moe_route_permute(A, 2 ** 30, 256, 6, *args) == UNSUPPORTED  # T*topk >= 2^31
+    assert lib.moe_route_permute(A, 100000, 1024, 1, *args) == UNSUPPORTED  # no room for block counts
+    assert lib.moe_route_permute(None, 8, 256, 6, *args) == NULL
+    assert lib.moe_route_permute(A, 8, 256, 6, U, A, A, A, A, None) == ALIGN
+
+
+def test_grouped_gemm_errors():
+    lib = _lib()
+
+    def call(**kw):
+        a = dict(q=A, qs=A, fmt=0, T=8, k=6, H=7168, I=2048, E=256, off=A, sp=A, w1=A, s1=A, w2=A, s2=A,
+                 h=A, hs=A, y=A, yd=1)
+        a.update(kw)
+        return lib.moe_grouped_mxfp4_gemm(a["q"], a["qs"], a["fmt"], a["T"], a["k"], a["H"], a["I"], a["E"],
+                                          a["off"], a["sp"], a["w1"], a["s1"], a["w2"], a["s2"], a["h"],
+                                          a["hs"], a["y"], a["yd"], None)
+
+    assert call(H=7168 + 128) == SHAPE
+    assert call(I=2048 + 32) == SHAPE
+    assert call(k=9) == SHAPE
+    assert call(fmt=5) == FORMAT
+    assert call(yd=3) == FORMAT
+    assert call(w2=None) == NULL
+    assert call(h=U) == ALIGN
+    assert call(E=4096) == UNSUPPORTED
+    assert call(T=0, q=None) == OK
+
+
+def test_combine_errors():
+    lib = _lib()
+    assert lib.moe_unpermute_combine(A, 1, A, A, 8, 6, 7164, A, 1, None) == SHAPE  # H % 8
+    assert lib.moe_unpermute_combine(A, 2, A, A, 8, 6, 7168, A, 1, None) == FORMAT
+    assert lib.moe_unpermute_combine(A, 1, None, A, 8, 6, 7168, A, 1, None) == NULL
+    assert lib.moe_unpermute_combine(A, 1, A, A, 8, 6, 7168, U, 1, None) == ALIGN
+    assert lib.moe_unpermute_combine(None, 1, None, None, 0, 6, 7168, None, 1, None) == OK

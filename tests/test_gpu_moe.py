@@ -1,0 +1,127 @@
+"""GPU parity of the MoE expert path: grouped FC1 (+ fused SwiGLU/requantise),
+FC2, combine, stage by stage and end to end, against the fp64 oracle.
+
+* h (requantised SwiGLU output): straddle rule against the oracle's own chain;
+* y (FC2): stage-isolated - the oracle's FC2 is fed the GPU's own h;
+* out (combine): stage-isolated on the GPU's y, and end to end against the
+  fully independent oracle chain; both within 2e-3 row-normalised.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp4_block_scaled_amd import datagen as dg
+from mxfp4_block_scaled_amd import ops
+from tests.helpers import GEMM_TOL, bf16_dev, host, straddle_check, unpack_codes
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_weights(w1, s1, w2, s2):
+    return [torch.from_numpy(np.ascontiguousarray(t)).cuda() for t in (w1, s1, w2, s2)]
+
+
+def _layer(x, logits, w, k, fmt, y_dtype=torch.bfloat16):
+    r = ops.moe_layer(bf16_dev(x), torch.from_numpy(logits).cuda(), *w, topk=k, act_fmt=fmt, y_dtype=y_dtype)
+    torch.cuda.synchronize()
+    return {name: host(t) for name, t in r.items()}
+
+
+def _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt, rows=None, tokens=None):
+    T = x.shape[0]
+    for key in ("q", "q_scale", "topk_ids", "expert_offsets", "sorted_pair", "pair_row"):
+        assert np.array_equal(g[key], ref[key]), key
+    rows = np.arange(T * k) if rows is None else np.asarray(rows)
+    # h: straddle rule against the oracle's fp64 pre-quantisation values
+    straddle_check(unpack_codes(g["h"][rows], fmt), g["h_scale"][rows], ref["h_pre"][rows], fmt)
+    # y: stage-isolated (oracle FC2 on the GPU's own h)
+    e_of_row = np.searchsorted(ref["expert_offsets"], rows, side="right") - 1
+    y_ref = np.zeros((rows.size, g["y"].shape[1]))
+    for e in np.unique(e_of_row):
+        sel = e_of_row == e
+        y_ref[sel] = oracle.fc2_rows(g["h"][rows[sel]], g["h_scale"][rows[sel]], fmt, w2[e], s2[e])
+    err_y = oracle.row_normalised_error(g["y"][rows], y_ref)
+    assert err_y <= GEMM_TOL, f"y error {err_y}"
+    # out: stage-isolated combine and end to end
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    gates = g["gates"].astype(np.float64)
+    y_full = np.zeros((T * k, g["y"].shape[1]))
+    y_full[rows] = g["y"][rows]
+    comb = oracle.combine(y_full, gates, g["pair_row"], T, k)
+    err_c = oracle.row_normalised_error(g["out"][tok], comb[tok])
+    assert err_c <= GEMM_TOL, f"combine error {err_c}"
+    err_e = oracle.row_normalised_error(g["out"][tok], ref["out"][tok])
+    assert err_e <= GEMM_TOL, f"end-to-end error {err_e}"
+    return err_y, err_c, err_e
+
+
+@pytest.mark.parametrize("T,H,I,E,k,fmt,seed", [
+    (8, 1024, 512, 16, 6, "e4m3", 0),      # decode-shaped: weight-streaming kernel
+    (40, 1536, 1024, 8, 3, "e2m1", 1),     # 40 tokens: streaming kernel, several rows per expert
+    (300, 1024, 512, 8, 6, "e4m3", 2),     # LDS-tiled kernel, several 128-row tiles, ragged tails
+    (333, 1024, 1024, 32, 4, "e2m1", 3),   # FP4 x FP4 tiles, some experts empty
+    (65, 512, 512, 4, 2, "e4m3", 4),       # just past the streaming threshold
+])
+def test_layer_small_shapes_full_oracle(T, H, I, E, k, fmt, seed):
+    x = dg.activations(seed, T, H)
+    logits = dg.logits(seed, T, E, "normal")
+    w1, s1, w2, s2 = dg.moe_weights(seed, E, H, I, 120, 128)
+    g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, fmt)
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, fmt)
+    _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt)
+
+
+def test_layer_skewed_routing_one_expert_takes_all():
+    T, H, I, E, k = 200, 512, 512, 8, 2
+    x = dg.activations(11, T, H)
+    logits = dg.logits(11, T, E, "normal")
+    logits[:, 5] += 50.0  # every token's first choice is expert 5 (two full tiles + a tail)
+    w1, s1, w2, s2 = dg.moe_weights(11, E, H, I, 120, 128)
+    g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, "e4m3")
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e4m3")
+    _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e4m3")
+
+
+def test_layer_fp32_y():
+    T, H, I, E, k = 24, 512, 512, 8, 3
+    x = dg.activations(12, T, H)
+    logits = dg.logits(12, T, E, "normal")
+    w1, s1, w2, s2 = dg.moe_weights(12, E, H, I, 120, 128)
+    g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, "e4m3", y_dtype=torch.float32)
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e4m3")
+    _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e4m3")
+
+
+@pytest.mark.parametrize("name,ntok", [("moe_decode_t8", None), ("moe_prefill_t2048_zipf", 6),
+                                        ("moe_prefill_t16384_fp4", 4)])
+def test_layer_workloads(name, ntok):
+    """Full-size layers; the oracle computes every row (decode) or the rows of a
+    token sample (prefill), including tokens routed to the hottest expert."""
+    d = dg.workload_inputs(name)
+    cfg = d["cfg"]
+    k, fmt = cfg["k"], cfg["act_fmt"]
+    w = (d["w1"], d["s1"], d["w2"], d["s2"])
+    g = _layer(d["x"], d["logits"], _dev_weights(*w), k, fmt)
+    if ntok is None:
+        ref = oracle.moe_layer(d["x"], d["logits"], *w, k, fmt)
+        _compare(g, ref, d["x"], d["logits"], *w, k, fmt)
+        return
+    T = cfg["T"]
+    rng = np.random.default_rng(7)
+    tokens = [0, T - 1] + list(rng.choice(np.arange(1, T - 1), ntok - 2, replace=False))
+    rows = [int(g["pair_row"][t * k + j]) for t in tokens for j in range(k)]
+    ref = oracle.moe_layer(d["x"], d["logits"], *w, k, fmt, rows=rows)
+    _compare(g, ref, d["x"], d["logits"], *w, k, fmt, rows=rows, tokens=tokens)
+
+
+def test_layer_is_deterministic():
+    T, H, I, E, k = 300, 1024, 512, 8, 6
+    x = bf16_dev(dg.activations(21, T, H))
+    logits = torch.from_numpy(dg.logits(21, T, E, "normal")).cuda()
+    w = _dev_weights(*dg.moe_weights(21, E, H, I, 120, 128))
+    a = ops.moe_layer(x, logits, *w, topk=k, act_fmt="e4m3")
+    b = ops.moe_layer(x, logits, *w, topk=k, act_fmt="e4m3")
+    for key in a:
+        assert torch.equal(a[key], b[key]), key

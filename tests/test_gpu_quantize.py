@@ -1,0 +1,86 @@
+"""GPU parity: mxfp4_quantize_act is bit-exact with the oracle (codes and scale bytes)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp4_block_scaled_amd import datagen as dg
+from mxfp4_block_scaled_amd import ops
+from tests.helpers import bf16_dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _adversarial_rows(K=256, seed=0):
+    """Rows that hit ties, saturation, zeros, -0, subnormals and extreme exponents."""
+    g = np.random.default_rng(seed)
+    rows = []
+    with open(os.path.join(os.path.dirname(__file__), "golden", "hand_blocks.json")) as f:
+        for blk in json.load(f)["blocks"]:
+            v = np.zeros(32, np.float32)
+            for i, (s, _c, _w) in enumerate(blk["elements"]):
+                v[i] = np.float32(float(s))
+            rows.append(v)
+    x = np.concatenate(rows + [np.zeros(32, np.float32)] * ((-len(rows)) % (K // 32)))
+    x = x.reshape(-1, K)
+    extra = []
+    # grid midpoints at many scales: value = (grid[i] + grid[i+1]) / 2 * 2^e
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 1.0625, 1.1875, 1.8125, 2.875])
+    for e in [-20, -8, -1, 0, 3, 11]:
+        v = np.resize(mids * 2.0 ** e, K) * g.choice([-1.0, 1.0], K)
+        extra.append(v)
+    extra.append(np.ldexp(g.random(K) + 0.5, g.integers(-140, 120, K)) * g.choice([-1.0, 1.0], K))
+    extra.append(np.where(g.random(K) < 0.5, -0.0, 0.0))
+    sub = (g.integers(1, 128, K).astype(np.uint32) << 16).view(np.float32)  # bf16 subnormals
+    extra.append(sub.astype(np.float64))
+    x = np.concatenate([x, np.array(extra)]).astype(np.float32)
+    return dg.bf16_bits_from_f32(x)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_quantize_adversarial_bit_exact(fmt):
+    bits = _adversarial_rows()
+    q, qs = ops.mxfp4_quantize_act(bf16_dev(bits), fmt)
+    ref_q, ref_s = oracle.moe.quantize_act(oracle.bf16_bits_to_f64(bits), fmt)
+    assert np.array_equal(host(qs), ref_s)
+    assert np.array_equal(host(q), ref_q)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_quantize_fp32_input_bit_exact(fmt):
+    g = np.random.default_rng(5)
+    x = (g.standard_normal((67, 512)) * np.exp2(g.integers(-30, 30, (67, 1)))).astype(np.float32)
+    x[3, 7] = -0.0
+    x[4, :32] = 0.0
+    x[5, :] = np.float32(1e-40)  # fp32 subnormals
+    q, qs = ops.mxfp4_quantize_act(torch.from_numpy(x).cuda(), fmt)
+    ref_q, ref_s = oracle.moe.quantize_act(x.astype(np.float64), fmt)
+    assert np.array_equal(host(qs), ref_s)
+    assert np.array_equal(host(q), ref_q)
+
+
+@pytest.mark.parametrize("name", ["moe_decode_t8", "moe_prefill_t2048_zipf", "moe_prefill_t16384_fp4"])
+def test_quantize_layer_inputs_bit_exact(name):
+    d = dg.workload_inputs(name, weights=False)
+    fmt = d["cfg"]["act_fmt"]
+    x = d["x"]
+    q, qs = ops.mxfp4_quantize_act(bf16_dev(x), fmt)
+    qh, sh = host(q), host(qs)
+    rows = np.unique(np.concatenate([np.arange(min(8, x.shape[0])),
+                                     np.random.default_rng(1).integers(0, x.shape[0], 256)]))
+    ref_q, ref_s = oracle.moe.quantize_act(oracle.bf16_bits_to_f64(x[rows]), fmt)
+    assert np.array_equal(sh[rows], ref_s)
+    assert np.array_equal(qh[rows], ref_q)
+
+
+def test_quantize_ragged_rows_and_empty():
+    bits = dg.activations(9, 3, 96)
+    q, qs = ops.mxfp4_quantize_act(bf16_dev(bits), "e4m3")
+    ref_q, ref_s = oracle.moe.quantize_act(oracle.bf16_bits_to_f64(bits), "e4m3")
+    assert np.array_equal(host(q), ref_q) and np.array_equal(host(qs), ref_s)
+    q0, s0 = ops.mxfp4_quantize_act(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), "e2m1")
+    assert q0.shape == (0, 32) and s0.shape == (0, 2)
