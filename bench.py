@@ -11,7 +11,11 @@ Also reported on the same line: the 8-token decode layer (weight GB/s over the
 touched experts) and the dense 64 x 4096 x 7168 GEMM, each against its roofline.
 The fp64 CPU oracle is timed on a bounded sample of the headline workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|decode|dense]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|decode|dense|copy]
+
+--only copy runs a plain device-to-device copy of 1 GiB per step (no JSON line):
+the reference kernel of known byte count that scales the FETCH_SIZE / WRITE_SIZE
+hardware counters into HBM bytes.
 """
 
 import argparse
@@ -224,13 +228,22 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "dense"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "dense", "copy"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the expert path here is the "
               "single-GPU kernel; no multi-GPU figure is measured.", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for i in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy: {args.warmup + args.steps} copies of {n} bytes")
+        return
     ops.load()
     torch.cuda.synchronize()
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

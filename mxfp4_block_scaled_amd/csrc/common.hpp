@@ -39,6 +39,17 @@ __device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b, v4f c, 
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Workgroup barrier for LDS hand-offs that leaves global loads in flight.
+// __syncthreads() makes the compiler drain every outstanding memory counter
+// (vmcnt included) first, which would cancel register prefetches issued for
+// later stages. Here only this wave's LDS operations are waited for (lgkmcnt),
+// which is what makes its LDS writes visible to the other waves after the
+// barrier; the asm's memory clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float wave_max16(float v) {
   // max over the 16 lanes that share l / 16 (butterfly inside each 16-lane row)
   v = fmaxf(v, __shfl_xor(v, 1));

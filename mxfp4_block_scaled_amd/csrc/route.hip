@@ -13,9 +13,9 @@
 // (built with LDS atomic ORs); across waves and blocks it is a prefix count.
 //
 // Small T (<= 256): one workgroup does everything in one launch.
-// Larger T: four launches - per-block top-k + per-block expert counts,
-// per-expert scan over blocks, ranks -> pair_row, and the inversion
-// pair_row -> sorted_pair. The per-block counts live in sorted_pair (used as
+// Larger T: five launches - top-k (a group of 16 or 64 lanes per token),
+// per-block expert counts, per-expert scan over blocks, ranks -> pair_row,
+// and the inversion pair_row -> sorted_pair. The per-block counts live in sorted_pair (used as
 // scratch) until the last launch overwrites it with the result, so the call
 // needs no workspace: this requires (nblocks + 1) * E <= T * k.
 #include "launch.hpp"
@@ -30,55 +30,68 @@ __device__ __forceinline__ bool beats(float x, int i, float y, int j) {
   return i >= 0 && (j < 0 || x > y || (x == y && i < j));
 }
 
-// top-S of one logits row, sorted; slots past the real ones keep id -1
-template <int S, bool kVec>
-__device__ __forceinline__ void topk_scan(const float* __restrict__ row, int E, float (&v)[S], int (&id)[S]) {
+// Top-k of one logits row by a group of L lanes (L = 16 or 64; 64 / L tokens per
+// wave). Lane j of the group holds logits e = j + L*i, i < 16 (E <= 16 L). Each
+// of the k rounds takes the group's best not-yet-taken (logit, index) pair with
+// a butterfly over the L lanes (higher logit first, then lower index).
+// Results are uniform across the group.
+template <int L>
+__device__ __forceinline__ void group_topk(const float* __restrict__ row, int E, int topk, bool active,
+                                           float (&val)[8], int (&id)[8]) {
+  const int j = threadIdx.x & (L - 1);
+  float v[16];
+  uint32_t taken = 0;
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    v[s] = 0.0f;
-    id[s] = -1;
+  for (int i = 0; i < 16; ++i) {
+    const int e = j + L * i;
+    v[i] = (active && e < E) ? row[e] : 0.0f;
+    if (!(active && e < E)) taken |= 1u << i;
   }
-  auto insert = [&](float x, int i) {
-    float c = x;
-    int ci = i;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const bool b = beats(c, ci, v[s], id[s]);
-      const float tv = v[s];
-      const int ti = id[s];
-      v[s] = b ? c : tv;
-      id[s] = b ? ci : ti;
-      c = b ? tv : c;
-      ci = b ? ti : ci;
+  for (int r = 0; r < 8; ++r) {
+    val[r] = 0.0f;
+    id[r] = -1;
+    if (r < topk) {
+      float bv = 0.0f;
+      int bi = -1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = j + L * i;
+        const bool ok = !((taken >> i) & 1u);
+        if (ok && beats(v[i], e, bv, bi)) {
+          bv = v[i];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int d = L / 2; d >= 1; d >>= 1) {
+        const float ov = __shfl_xor(bv, d);
+        const int oi = __shfl_xor(bi, d);
+        if (beats(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if (bi >= 0 && (bi & (L - 1)) == j) taken |= 1u << (bi / L);
+      val[r] = bv;
+      id[r] = bi;
     }
-  };
-  if (kVec) {
-    for (int e = 0; e < E; e += 4) {
-      const float4 f = *reinterpret_cast<const float4*>(row + e);
-      insert(f.x, e);
-      insert(f.y, e + 1);
-      insert(f.z, e + 2);
-      insert(f.w, e + 3);
-    }
-  } else {
-    for (int e = 0; e < E; ++e) insert(row[e], e);
   }
 }
 
-template <int S>
-__device__ __forceinline__ void write_route(int64_t t, int topk, const float (&v)[S], const int (&id)[S],
+__device__ __forceinline__ void write_route(int64_t t, int topk, const float (&v)[8], const int (&id)[8],
                                             int32_t* __restrict__ topk_ids, float* __restrict__ gates) {
-  float z[S];
+  float z[8];
   float sum = 0.0f;
 #pragma unroll
-  for (int j = 0; j < S; ++j) {
+  for (int j = 0; j < 8; ++j) {
     if (j < topk) {
       z[j] = expf(v[j] - v[0]);
       sum += z[j];
     }
   }
 #pragma unroll
-  for (int j = 0; j < S; ++j) {
+  for (int j = 0; j < 8; ++j) {
     if (j < topk) {
       topk_ids[t * topk + j] = id[j];
       gates[t * topk + j] = z[j] / sum;
@@ -86,7 +99,8 @@ __device__ __forceinline__ void write_route(int64_t t, int topk, const float (&v
   }
 }
 
-// exclusive scan over the 256 threads of a block; tmp: 4 ints of LDS
+// exclusive scan over the NW waves of a block; tmp: NW ints of LDS
+template <int NW = 4>
 __device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int incl = x;
@@ -99,7 +113,7 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int* total)
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NW; ++i) {
     base += (i < w) ? tmp[i] : 0;
     tot += tmp[i];
   }
@@ -115,94 +129,98 @@ __device__ __forceinline__ int wave_rank(const unsigned long long* bits, int E, 
   return r + __popcll(bits[w * E + e] & ((1ull << lane) - 1ull));
 }
 
-template <int S, bool kVec>
-__global__ void __launch_bounds__(kRouteThreads) route_small_kernel(
+constexpr int kSmallThreads = 1024;
+
+// T <= 256: one workgroup of 16 waves. Phase 1: top-k by lane groups; phase 2:
+// thread t < T builds the per-wave expert masks; then counts, scan and ranks.
+template <int L>
+__global__ void __launch_bounds__(kSmallThreads) route_small_kernel(
     const float* __restrict__ logits, int T, int E, int topk, int32_t* __restrict__ topk_ids,
     float* __restrict__ gates, int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_pair,
     int32_t* __restrict__ pair_row) {
-  extern __shared__ unsigned long long bits[];  // [4][E]
+  extern __shared__ unsigned long long bits[];  // [4][E]: tokens 0..255 in 4 mask words
+  __shared__ int sids[kSmallT * 8];
   __shared__ int offs[1025];
-  __shared__ int tmp[4];
+  __shared__ int tmp[16];
+  constexpr int TPW = 64 / L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int i = tid; i < 4 * E; i += kRouteThreads) bits[i] = 0ull;
-  __syncthreads();
-  float v[S];
-  int id[S];
-  const bool valid = tid < T;
-  if (valid) {
-    topk_scan<S, kVec>(logits + (int64_t)tid * E, E, v, id);
-    write_route<S>(tid, topk, v, id, topk_ids, gates);
+  for (int i = tid; i < 4 * E; i += kSmallThreads) bits[i] = 0ull;
+  const int grp = w * TPW + lane / L;
+  for (int t0 = 0; t0 < T; t0 += 16 * TPW) {
+    const int t = t0 + grp;
+    const bool active = t < T;
+    float val[8];
+    int id[8];
+    group_topk<L>(logits + (int64_t)(active ? t : 0) * E, E, topk, active, val, id);
+    if (active && (lane & (L - 1)) == 0) {
+      write_route(t, topk, val, id, topk_ids, gates);
 #pragma unroll
-    for (int j = 0; j < S; ++j)
-      if (j < topk) atomicOr(&bits[w * E + id[j]], 1ull << lane);
+      for (int j = 0; j < 8; ++j)
+        if (j < topk) sids[t * topk + j] = id[j];
+    }
   }
   __syncthreads();
-  // per-expert totals and their exclusive scan (thread owns experts [tid*C, tid*C+C))
-  const int C = (E + kRouteThreads - 1) / kRouteThreads;
-  int local = 0;
-  for (int i = 0; i < C; ++i) {
-    const int e = tid * C + i;
-    if (e < E) {
-      int c = 0;
-      for (int ww = 0; ww < 4; ++ww) c += __popcll(bits[ww * E + e]);
-      local += c;
-    }
+  if (tid < T) {
+    for (int j = 0; j < topk; ++j) atomicOr(&bits[(tid >> 6) * E + sids[tid * topk + j]], 1ull << lane);
   }
+  __syncthreads();
+  int c = 0;
+  if (tid < E)
+    for (int ww = 0; ww < 4; ++ww) c += __popcll(bits[ww * E + tid]);
   int total;
-  int base = block_exclusive_scan(local, tmp, &total);
-  for (int i = 0; i < C; ++i) {
-    const int e = tid * C + i;
-    if (e < E) {
-      int c = 0;
-      for (int ww = 0; ww < 4; ++ww) c += __popcll(bits[ww * E + e]);
-      offs[e] = base;
-      expert_offsets[e] = base;
-      base += c;
-    }
+  const int base = block_exclusive_scan<16>(c, tmp, &total);
+  if (tid < E) {
+    offs[tid] = base;
+    expert_offsets[tid] = base;
   }
   if (tid == 0) {
     offs[E] = total;
     expert_offsets[E] = total;
   }
   __syncthreads();
-  if (valid) {
-#pragma unroll
-    for (int j = 0; j < S; ++j) {
-      if (j < topk) {
-        const int e = id[j];
-        const int r = offs[e] + wave_rank(bits, E, e);
-        const int p = tid * topk + j;
-        pair_row[p] = r;
-        sorted_pair[r] = p;
-      }
+  if (tid < T) {
+    for (int j = 0; j < topk; ++j) {
+      const int e = sids[tid * topk + j];
+      const int r = offs[e] + wave_rank(bits, E, e);
+      const int p = tid * topk + j;
+      pair_row[p] = r;
+      sorted_pair[r] = p;
     }
   }
 }
 
-// large T, launch 1: top-k of 256 tokens per block + the block's expert counts
-template <int S, bool kVec>
-__global__ void __launch_bounds__(kRouteThreads) route_count_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int topk, int32_t* __restrict__ topk_ids,
-    float* __restrict__ gates, int32_t* __restrict__ scratch) {
+// large T, launch 1: top-k, one token per group of L lanes (64 / L tokens per wave)
+template <int L>
+__global__ void __launch_bounds__(kRouteThreads) route_topk_kernel(const float* __restrict__ logits, int64_t T,
+                                                                   int E, int topk, int32_t* __restrict__ topk_ids,
+                                                                   float* __restrict__ gates) {
+  constexpr int TPB = kRouteThreads / L;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x / L;
+  const bool active = t < T;
+  float val[8];
+  int id[8];
+  group_topk<L>(logits + (active ? t : 0) * E, E, topk, active, val, id);
+  if (active && (lane & (L - 1)) == 0) write_route(t, topk, val, id, topk_ids, gates);
+}
+
+// large T, launch 2: the expert counts of each block of 256 tokens
+__global__ void __launch_bounds__(kRouteThreads) route_count_kernel(const int32_t* __restrict__ topk_ids,
+                                                                    int64_t T, int E, int topk,
+                                                                    int32_t* __restrict__ scratch) {
   extern __shared__ int cnt[];  // [E]
   const int tid = threadIdx.x;
   for (int i = tid; i < E; i += kRouteThreads) cnt[i] = 0;
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * kRouteThreads + tid;
   if (t < T) {
-    float v[S];
-    int id[S];
-    topk_scan<S, kVec>(logits + t * E, E, v, id);
-    write_route<S>(t, topk, v, id, topk_ids, gates);
-#pragma unroll
-    for (int j = 0; j < S; ++j)
-      if (j < topk) atomicAdd(&cnt[id[j]], 1);
+    for (int j = 0; j < topk; ++j) atomicAdd(&cnt[topk_ids[t * topk + j]], 1);
   }
   __syncthreads();
   for (int i = tid; i < E; i += kRouteThreads) scratch[(int64_t)blockIdx.x * E + i] = cnt[i];
 }
 
-// large T, launch 2: block e turns column e of the counts into exclusive prefixes
+// large T, launch 3: block e turns column e of the counts into exclusive prefixes
 // over blocks and stores the expert total in row nblk
 __global__ void __launch_bounds__(kRouteThreads) route_scan_kernel(int32_t* __restrict__ scratch, int nblk, int E) {
   __shared__ int tmp[4];
@@ -226,7 +244,7 @@ __global__ void __launch_bounds__(kRouteThreads) route_scan_kernel(int32_t* __re
   if (tid == 0) scratch[(int64_t)nblk * E + e] = total;
 }
 
-// large T, launch 3: expert offsets (every block rescans the E totals) and ranks
+// large T, launch 4: expert offsets (every block rescans the E totals) and ranks
 __global__ void __launch_bounds__(kRouteThreads) route_rank_kernel(
     const int32_t* __restrict__ topk_ids, int64_t T, int E, int topk, int nblk,
     const int32_t* __restrict__ scratch, int32_t* __restrict__ expert_offsets,
@@ -282,7 +300,7 @@ __global__ void __launch_bounds__(kRouteThreads) route_rank_kernel(
   }
 }
 
-// large T, launch 4: sorted_pair = inverse of pair_row (overwrites the scratch)
+// large T, launch 5: sorted_pair = inverse of pair_row (overwrites the scratch)
 __global__ void __launch_bounds__(kRouteThreads) invert_kernel(const int32_t* __restrict__ pair_row, int64_t n,
                                                                int32_t* __restrict__ sorted_pair) {
   const int64_t p = (int64_t)blockIdx.x * kRouteThreads + threadIdx.x;
@@ -295,28 +313,20 @@ int route_permute_supported(int64_t T, int E, int topk) {
   return (nblk + 1) * (int64_t)E <= T * topk ? 1 : 0;
 }
 
-template <int S>
-static void launch_route_s(const float* logits, int64_t T, int E, int topk, int32_t* topk_ids, float* gates,
-                           int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_row, bool vec,
-                           hipStream_t stream) {
+template <int L>
+static void launch_route_l(const float* logits, int64_t T, int E, int topk, int32_t* topk_ids, float* gates,
+                           int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_row, hipStream_t stream) {
   const size_t bits_bytes = sizeof(unsigned long long) * 4 * E;
   if (T <= kSmallT) {
-    if (vec)
-      route_small_kernel<S, true><<<1, kRouteThreads, bits_bytes, stream>>>(
-          logits, (int)T, E, topk, topk_ids, gates, expert_offsets, sorted_pair, pair_row);
-    else
-      route_small_kernel<S, false><<<1, kRouteThreads, bits_bytes, stream>>>(
-          logits, (int)T, E, topk, topk_ids, gates, expert_offsets, sorted_pair, pair_row);
+    route_small_kernel<L><<<1, kSmallThreads, bits_bytes, stream>>>(logits, (int)T, E, topk, topk_ids, gates,
+                                                                     expert_offsets, sorted_pair, pair_row);
     return;
   }
   const int nblk = (int)cdiv(T, kRouteThreads);
   int32_t* scratch = sorted_pair;
-  if (vec)
-    route_count_kernel<S, true><<<nblk, kRouteThreads, sizeof(int) * E, stream>>>(logits, T, E, topk, topk_ids,
-                                                                                   gates, scratch);
-  else
-    route_count_kernel<S, false><<<nblk, kRouteThreads, sizeof(int) * E, stream>>>(logits, T, E, topk, topk_ids,
-                                                                                    gates, scratch);
+  constexpr int TPB = kRouteThreads / L;
+  route_topk_kernel<L><<<(unsigned)cdiv(T, TPB), kRouteThreads, 0, stream>>>(logits, T, E, topk, topk_ids, gates);
+  route_count_kernel<<<nblk, kRouteThreads, sizeof(int) * E, stream>>>(topk_ids, T, E, topk, scratch);
   route_scan_kernel<<<E, kRouteThreads, 0, stream>>>(scratch, nblk, E);
   route_rank_kernel<<<nblk, kRouteThreads, bits_bytes, stream>>>(topk_ids, T, E, topk, nblk, scratch,
                                                                  expert_offsets, pair_row);
@@ -327,11 +337,10 @@ static void launch_route_s(const float* logits, int64_t T, int E, int topk, int3
 int launch_route_permute(const float* logits, int64_t T, int E, int topk, int32_t* topk_ids, float* gates,
                          int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_row,
                          hipStream_t stream) {
-  const bool vec = (E % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
-  if (topk <= 6)
-    launch_route_s<6>(logits, T, E, topk, topk_ids, gates, expert_offsets, sorted_pair, pair_row, vec, stream);
+  if (E <= 256)
+    launch_route_l<16>(logits, T, E, topk, topk_ids, gates, expert_offsets, sorted_pair, pair_row, stream);
   else
-    launch_route_s<8>(logits, T, E, topk, topk_ids, gates, expert_offsets, sorted_pair, pair_row, vec, stream);
+    launch_route_l<64>(logits, T, E, topk, topk_ids, gates, expert_offsets, sorted_pair, pair_row, stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
