@@ -39,6 +39,22 @@ PEAK_TFLOPS = {"e2m1": 10100.0, "e4m3": 5000.0}  # dense MXFP4 / MXFP8 (FP8 x FP
 FLOP_PER_PAIR = 2 * 7168 * 4096 + 2 * 2048 * 7168  # 88,080,384
 BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,352
 
+# HBM bytes per grouped-GEMM call (FC1 + FC2 launches) from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes, scaled by a 1 GiB copy (2.0 x FETCH_SIZE + 1.0 x WRITE_SIZE; the passes and the
+# calibration are in profiles/moe_layer_hbm_traffic.md). They hold only for the GEMM source
+# they were measured on: on any other source the roofline reports traffic = null.
+TRAFFIC_SRC_SHA256 = "123f63900cb781546edffd7c1c0063debe44c5e96bd57712476ed576aca57969"
+TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 12361979904, "moe_decode_t8": 1030335488}
+
+
+def measured_traffic(workload):
+    import hashlib
+    src = os.path.join(ROOT, "mxfp4_block_scaled_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != TRAFFIC_SRC_SHA256:
+            return None
+    return TRAFFIC_BYTES.get(workload)
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -266,7 +282,7 @@ def main():
             "stages_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
             "roofline": {"kernel": "moe_grouped_mxfp4_gemm (FC1 + FC2 kernels)", "bound": "mfma",
                          "achieved": round(g_tflops, 3), "peak": peak, "unit": "TFLOP/s",
-                         "frac": round(g_tflops / peak, 4), "traffic": None},
+                         "frac": round(g_tflops / peak, 4), "traffic": measured_traffic(name)},
         })
         del r["layer"]
         torch.cuda.empty_cache()
@@ -282,7 +298,7 @@ def main():
                "roofline": {"kernel": "moe_grouped_mxfp4_gemm (FC1 + FC2 kernels)", "bound": "hbm",
                             "achieved": round(r["wbytes"] / (g_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(r["wbytes"] / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                            "traffic": None}}
+                            "traffic": measured_traffic(name)}}
         if "value" not in result:
             result.update({"value": dec["weight_GBps_layer"], "unit": "GB/s", "ms_per_step": dec["ms_per_step"],
                            "dtype": "mxfp8 x mxfp4 (e4m3 x e2m1, fp32 accumulate)",
