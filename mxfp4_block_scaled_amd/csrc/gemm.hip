@@ -163,6 +163,19 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
 
 // ---------------------------------------------------------------------------------
 // weight-streaming kernel (rows per expert <= 16 * MT)
+//
+// K order inside a 512-k super-step: step s, hardware block hb <-> memory block
+// 4 s + hb. Then the 4 lane groups of a row read 64 contiguous bytes per load
+// instruction (16 bytes each, FP4), and an FP8 lane's two 16-byte halves sit at
+// 128 s + 16 g and 128 s + 64 + 16 g. The scale of (row, block 4 s + g) is byte
+// 4 s + g of the row's 16 scale bytes, so a lane gathers bytes g, 4+g, 8+g and
+// 12+g of them into one register (op_sel = s picks byte s).
+__device__ __forceinline__ int gather_scales(v4i d, int g) {
+  const int sh = 8 * g;
+  return (int)((((uint32_t)d[0] >> sh) & 0xFFu) | ((((uint32_t)d[1] >> sh) & 0xFFu) << 8) |
+               ((((uint32_t)d[2] >> sh) & 0xFFu) << 16) | ((((uint32_t)d[3] >> sh) & 0xFFu) << 24));
+}
+
 template <bool kActFP4, int kMode, bool kYBF16, int MT>
 __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
   constexpr int kFA = kActFP4 ? kFmtFP4 : kFmtFP8;
@@ -201,8 +214,8 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
       fvalid[f] = n < a.N;
     }
     const int64_t nr = n + r16;
-    wp[f] = a.w + ((int64_t)e * a.N + nr) * wrow_bytes + 64 * g;
-    sp[f] = a.w_scale + ((int64_t)e * a.N + nr) * srow_bytes + 4 * g;
+    wp[f] = a.w + ((int64_t)e * a.N + nr) * wrow_bytes + 16 * g;
+    sp[f] = a.w_scale + ((int64_t)e * a.N + nr) * srow_bytes;
   }
   // activation rows of the MT fragments
   const uint8_t* ap[MT];
@@ -217,8 +230,8 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
       if (kMode == kModeFC1) src = a.sorted_pair[row0 + lr] / a.topk;
       else src = row0 + lr;
     }
-    ap[mt] = a.act + src * arow_bytes;
-    asp[mt] = a.act_scale + src * srow_bytes + 4 * g;
+    ap[mt] = a.act + src * arow_bytes + 16 * g;
+    asp[mt] = a.act_scale + src * srow_bytes;
   }
 
   v4f acc[MT][4];
@@ -235,10 +248,10 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       if (fvalid[f]) {
-        const v4i* src = reinterpret_cast<const v4i*>(wp[f] + (int64_t)ss * 256);
+        const uint8_t* src = wp[f] + (int64_t)ss * 256;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bq[f][s] = __builtin_nontemporal_load(src + s);
-        bs[f] = *reinterpret_cast<const int*>(sp[f] + (int64_t)ss * 16);
+        for (int s = 0; s < 4; ++s) bq[f][s] = *reinterpret_cast<const v4i*>(src + 64 * s);
+        bs[f] = gather_scales(*reinterpret_cast<const v4i*>(sp[f] + (int64_t)ss * 16), g);
       } else {
 #pragma unroll
         for (int s = 0; s < 4; ++s) bq[f][s] = v4i{0, 0, 0, 0};
@@ -251,22 +264,22 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
       int as = 0;
       if (avalid[mt]) {
         if (kActFP4) {
-          const v4i* src = reinterpret_cast<const v4i*>(ap[mt] + (int64_t)ss * 256 + 64 * g);
+          const uint8_t* src = ap[mt] + (int64_t)ss * 256;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            v4i x = src[s];
+            v4i x = *reinterpret_cast<const v4i*>(src + 64 * s);
             aq[s] = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
           }
         } else {
-          const uint8_t* base = ap[mt] + (int64_t)ss * 512 + 128 * (g >> 1) + 16 * (g & 1);
+          const uint8_t* base = ap[mt] + (int64_t)ss * 512;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            v4i lo = *reinterpret_cast<const v4i*>(base + 32 * s);
-            v4i hi = *reinterpret_cast<const v4i*>(base + 256 + 32 * s);
+            v4i lo = *reinterpret_cast<const v4i*>(base + 128 * s);
+            v4i hi = *reinterpret_cast<const v4i*>(base + 128 * s + 64);
             aq[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           }
         }
-        as = *reinterpret_cast<const int*>(asp[mt] + (int64_t)ss * 16);
+        as = gather_scales(*reinterpret_cast<const v4i*>(asp[mt] + (int64_t)ss * 16), g);
       } else {
 #pragma unroll
         for (int s = 0; s < 4; ++s) aq[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
