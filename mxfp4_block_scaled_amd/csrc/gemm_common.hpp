@@ -1,0 +1,177 @@
+// Shared pieces of the MXFP4 GEMM kernels (weight-streaming and LDS-ring):
+// the argument block, the expert/work-unit lookup over expert_offsets, the
+// 32x32x64 scaled MFMA, the per-32 requantisation of one staged row block, and
+// the HBM -> LDS copy and wait primitives.
+//
+// The weights stay E2M1 + UE8M0 all the way into the matrix instruction - no
+// dequantisation to a 16-bit type (page "DGX Spark 原生 FP4 矩阵指令" sections 一
+// and 二). Activations are E4M3 (FP8 x FP4) or E2M1 (FP4 x FP4); products are
+// exact and accumulate in fp32. FC1's epilogue fuses SwiGLU and the
+// requantisation of h per 32 along I (page "Domestic GPUs are awesome! ...
+// DeepSeek-V4": "SwiGLU + FP8 quant").
+#pragma once
+
+#include <type_traits>
+
+#include "launch.hpp"
+#include "mx_codec.hpp"
+
+namespace mxf {
+
+enum { kModeFC1 = 0, kModeFC2 = 1, kModeDense = 2 };
+
+struct GemmArgs {
+  const uint8_t* act;        // FC1: q [T][K(/2)], FC2: h [R][K(/2)], dense: qa [M][K(/2)]
+  const uint8_t* act_scale;  // [.][K/32]
+  const uint8_t* w;          // [E][N][K/2]
+  const uint8_t* w_scale;    // [E][N][K/32]
+  const int32_t* offsets;    // [E+1] (FC1/FC2)
+  const int32_t* sorted_pair;
+  uint8_t* h;                // FC1 out [R][I(/2)]
+  uint8_t* h_scale;          // FC1 out [R][I/32]
+  void* out;                 // FC2: y [R][N]; dense: c [M][N]
+  int64_t K, N, I, M;
+  int topk, E;
+  int ntiles;  // tile kernel: weight-row tiles per expert (1-D grid: block = m_unit * ntiles + n_tile)
+};
+
+// ---------------------------------------------------------------------------------
+// Which expert does work unit u belong to? units(e) = (count_e > 0) when BM == 0,
+// else ceil(count_e / BM). Called by a whole wave; results are wave-uniform.
+template <int BM>
+__device__ __forceinline__ int units_of(int c) {
+  if constexpr (BM == 0) return c > 0 ? 1 : 0;
+  else return (c + BM - 1) / BM;
+}
+
+template <int BM>
+__device__ __forceinline__ void find_unit(const int32_t* __restrict__ off, int E, int u, int& e_out, int& loc_out) {
+  const int lane = threadIdx.x & 63;
+  const int C = (E + 63) >> 6;
+  const int first = lane * C;
+  int units = 0;
+  for (int i = 0; i < C; ++i) {
+    const int e = first + i;
+    if (e < E) {
+      const int c = off[e + 1] - off[e];
+      units += units_of<BM>(c);
+    }
+  }
+  int incl = units;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  const int excl = incl - units;
+  const bool mine = u >= excl && u < incl;
+  const unsigned long long m = __ballot(mine);
+  if (m == 0) {
+    e_out = -1;
+    loc_out = 0;
+    return;
+  }
+  const int src = __ffsll((long long)m) - 1;
+  int ee = -1, loc = 0;
+  if (mine) {
+    int acc = excl;
+    for (int i = 0; i < C; ++i) {
+      const int e = first + i;
+      if (e < E) {
+        const int c = off[e + 1] - off[e];
+        const int n = units_of<BM>(c);
+        if (u < acc + n) {
+          ee = e;
+          loc = u - acc;
+          break;
+        }
+        acc += n;
+      }
+    }
+  }
+  e_out = __shfl(ee, src);
+  loc_out = __shfl(loc, src);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+template <bool kYBF16>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
+  if (kYBF16)
+    static_cast<uint16_t*>(out)[idx] = (uint16_t)bf16_round(x);
+  else
+    static_cast<float*>(out)[idx] = x;
+}
+
+template <int FA, int FB, int OPS>
+__device__ __forceinline__ v16f mfma32x32x64(const v8i& a, const v8i& b, v16f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, OPS, sa, OPS, sb);
+}
+
+// Quantise 32 consecutive fp32 values (one block of a row) held by one thread and
+// store codes + scale byte; used by the staged FC1 epilogue.
+template <bool kActFP4>
+__device__ __forceinline__ void quantize_store32(const float* __restrict__ src, uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ scale) {
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    const float4 f = *reinterpret_cast<const float4*>(src + i);
+    v[i] = f.x;
+    v[i + 1] = f.y;
+    v[i + 2] = f.z;
+    v[i + 3] = f.w;
+  }
+  uint32_t out[8];
+  const uint32_t byte = quantize_block32<kActFP4>(v, out);
+  if (kActFP4) {
+    *reinterpret_cast<uint4*>(codes) = make_uint4(out[0], out[1], out[2], out[3]);
+  } else {
+    reinterpret_cast<uint4*>(codes)[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    reinterpret_cast<uint4*>(codes)[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  }
+  *scale = (uint8_t)byte;
+}
+
+
+// swizzle of the 16-byte chunk index inside a row (8 or 16 chunks per row)
+template <int C>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (C == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return r & 15;
+}
+
+// HBM -> LDS copy of 16 (or 4) bytes per lane: lane l lands at lds + 16 l (4 l).
+// The builtins below exist only for the device pass of the compiler.
+__device__ __forceinline__ void dma16_to_lds(const void* src, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+__device__ __forceinline__ void dma4_to_lds(const void* src, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+#endif
+}
+
+// wait until at most N vector-memory loads of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+#endif
+}
+
+// tile geometry of the LDS-ring kernels: 128 activation rows x 256 weight rows
+namespace tile {
+constexpr int BM = 128, BN = 256;
+}  // namespace tile
+
+// kernel launchers (gemm_stream.hip, gemm_tile.hip); mode is kModeFC1 / kModeFC2 / kModeDense
+void launch_stream_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int mt, dim3 grid,
+                        hipStream_t stream);
+void launch_tile_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int64_t m_units,
+                      hipStream_t stream);
+
+}  // namespace mxf

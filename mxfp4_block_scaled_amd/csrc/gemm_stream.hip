@@ -1,0 +1,248 @@
+// Weight-streaming MXFP4 GEMM for few rows per expert (decode, small dense M):
+// weights go straight from HBM to registers in the 16x16x128 scaled MFMA's lane
+// layout, the K range is split over the 4 waves of a workgroup and reduced
+// through LDS in a fixed order. One workgroup = one expert x 64 weight rows
+// (FC1: 32 gate + the 32 matching up rows, so SwiGLU stays local).
+#include "gemm_common.hpp"
+
+namespace mxf {
+
+// FC1 epilogue for one 16-row m-fragment held as tot[f][v], f = gate0, gate1, up0, up1,
+// lane (g = l/16, r16 = l%16): row 4g+v, column i_base + 16*(f&1) + r16.
+// The 32 columns [i_base, i_base+32) form exactly one quantisation block.
+template <bool kActFP4>
+__device__ __forceinline__ void epilogue_fc1(const float (&tot)[4][4], int local_row0, int m_valid, int64_t row_base,
+                                             int64_t i_base, int64_t I, uint8_t* __restrict__ h,
+                                             uint8_t* __restrict__ h_scale) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float hv[2];
+    hv[0] = silu_mul(tot[0][v], tot[2][v]);
+    hv[1] = silu_mul(tot[1][v], tot[3][v]);
+    uint32_t amax = max(__float_as_uint(hv[0]) & 0x7FFFFFFFu, __float_as_uint(hv[1]) & 0x7FFFFFFFu);
+    amax = __float_as_uint(wave_max16(__uint_as_float(amax)));
+    const uint32_t byte = scale_byte_from_amax_bits(amax, kActFP4 ? kEmaxE2M1 : kEmaxE4M3);
+    const float inv = inv_scale_from_byte(byte);
+    uint32_t code[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) code[c] = kActFP4 ? e2m1_code(hv[c], inv) : e4m3_code(hv[c], inv);
+    uint32_t pair[2];
+    if (kActFP4) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) pair[c] = code[c] | (__shfl_xor(code[c], 1) << 4);
+    }
+    const int lr = local_row0 + 4 * g + v;
+    if (lr < m_valid) {
+      const int64_t R = row_base + lr;
+      if (kActFP4) {
+        if ((r16 & 1) == 0) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) h[R * (I / 2) + (i_base + 16 * c + r16) / 2] = (uint8_t)pair[c];
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) h[R * I + i_base + 16 * c + r16] = (uint8_t)code[c];
+      }
+      if (r16 == 0) h_scale[R * (I / 32) + i_base / 32] = (uint8_t)byte;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// weight-streaming kernel (rows per expert <= 16 * MT)
+//
+// K order inside a 512-k super-step: step s, hardware block hb <-> memory block
+// 4 s + hb. Then the 4 lane groups of a row read 64 contiguous bytes per load
+// instruction (16 bytes each, FP4), and an FP8 lane's two 16-byte halves sit at
+// 128 s + 16 g and 128 s + 64 + 16 g. The scale of (row, block 4 s + g) is byte
+// 4 s + g of the row's 16 scale bytes, so a lane gathers bytes g, 4+g, 8+g and
+// 12+g of them into one register (op_sel = s picks byte s).
+__device__ __forceinline__ int gather_scales(v4i d, int g) {
+  const int sh = 8 * g;
+  return (int)((((uint32_t)d[0] >> sh) & 0xFFu) | ((((uint32_t)d[1] >> sh) & 0xFFu) << 8) |
+               ((((uint32_t)d[2] >> sh) & 0xFFu) << 16) | ((((uint32_t)d[3] >> sh) & 0xFFu) << 24));
+}
+
+template <bool kActFP4, int kMode, bool kYBF16, int MT>
+__global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
+  constexpr int kFA = kActFP4 ? kFmtFP4 : kFmtFP8;
+  __shared__ float red[4][MT * 16][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+
+  int e = 0;
+  int64_t row0 = 0;
+  int m = 0;
+  if (kMode == kModeDense) {
+    m = (int)a.M;
+  } else {
+    int loc;
+    find_unit<0>(a.offsets, a.E, blockIdx.y, e, loc);
+    if (e < 0) return;
+    row0 = a.offsets[e];
+    m = a.offsets[e + 1] - (int)row0;
+  }
+  const int64_t K = a.K;
+  const int64_t wrow_bytes = K / 2, srow_bytes = K / 32;
+  const int64_t arow_bytes = kActFP4 ? K / 2 : K;
+
+  // the 4 weight fragments of this workgroup
+  const uint8_t* wp[4];
+  const uint8_t* sp[4];
+  bool fvalid[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    int64_t n;
+    if (kMode == kModeFC1) {
+      const int64_t i0 = (int64_t)blockIdx.x * 32 + 16 * (f & 1);
+      n = (f < 2 ? 0 : a.I) + i0;
+      fvalid[f] = true;
+    } else {
+      n = (int64_t)blockIdx.x * 64 + 16 * f;
+      fvalid[f] = n < a.N;
+    }
+    const int64_t nr = n + r16;
+    wp[f] = a.w + ((int64_t)e * a.N + nr) * wrow_bytes + 16 * g;
+    sp[f] = a.w_scale + ((int64_t)e * a.N + nr) * srow_bytes;
+  }
+  // activation rows of the MT fragments
+  const uint8_t* ap[MT];
+  const uint8_t* asp[MT];
+  bool avalid[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int lr = 16 * mt + r16;
+    avalid[mt] = lr < m;
+    int64_t src = 0;
+    if (avalid[mt]) {
+      if (kMode == kModeFC1) src = a.sorted_pair[row0 + lr] / a.topk;
+      else src = row0 + lr;
+    }
+    ap[mt] = a.act + src * arow_bytes + 16 * g;
+    asp[mt] = a.act_scale + src * srow_bytes;
+  }
+
+  v4f acc[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[mt][f] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int nss = (int)(K / 512);
+  const int ss_begin = wave * nss / 4, ss_end = (wave + 1) * nss / 4;
+  for (int ss = ss_begin; ss < ss_end; ++ss) {
+    v4i bq[4][4];
+    int bs[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if (fvalid[f]) {
+        const uint8_t* src = wp[f] + (int64_t)ss * 256;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bq[f][s] = *reinterpret_cast<const v4i*>(src + 64 * s);
+        bs[f] = gather_scales(*reinterpret_cast<const v4i*>(sp[f] + (int64_t)ss * 16), g);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bq[f][s] = v4i{0, 0, 0, 0};
+        bs[f] = 0;
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      v8i aq[4];
+      int as = 0;
+      if (avalid[mt]) {
+        if (kActFP4) {
+          const uint8_t* src = ap[mt] + (int64_t)ss * 256;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            v4i x = *reinterpret_cast<const v4i*>(src + 64 * s);
+            aq[s] = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+          }
+        } else {
+          const uint8_t* base = ap[mt] + (int64_t)ss * 512;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            v4i lo = *reinterpret_cast<const v4i*>(base + 128 * s);
+            v4i hi = *reinterpret_cast<const v4i*>(base + 128 * s + 64);
+            aq[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+        }
+        as = gather_scales(*reinterpret_cast<const v4i*>(asp[mt] + (int64_t)ss * 16), g);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) aq[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        v8i b0 = v8i{bq[f][0][0], bq[f][0][1], bq[f][0][2], bq[f][0][3], 0, 0, 0, 0};
+        v8i b1 = v8i{bq[f][1][0], bq[f][1][1], bq[f][1][2], bq[f][1][3], 0, 0, 0, 0};
+        v8i b2 = v8i{bq[f][2][0], bq[f][2][1], bq[f][2][2], bq[f][2][3], 0, 0, 0, 0};
+        v8i b3 = v8i{bq[f][3][0], bq[f][3][1], bq[f][3][2], bq[f][3][3], 0, 0, 0, 0};
+        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 0>(aq[0], b0, acc[mt][f], as, bs[f]);
+        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 1>(aq[1], b1, acc[mt][f], as, bs[f]);
+        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 2>(aq[2], b2, acc[mt][f], as, bs[f]);
+        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 3>(aq[3], b3, acc[mt][f], as, bs[f]);
+      }
+    }
+  }
+
+  // reduce the 4 K-slices in a fixed order (deterministic)
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave][mt * 16 + f * 4 + v][lane] = acc[mt][f][v];
+  __syncthreads();
+  for (int mt = wave; mt < MT; mt += 4) {
+    float tot[4][4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int idx = mt * 16 + f * 4 + v;
+        tot[f][v] = ((red[0][idx][lane] + red[1][idx][lane]) + red[2][idx][lane]) + red[3][idx][lane];
+      }
+    if (kMode == kModeFC1) {
+      epilogue_fc1<kActFP4>(tot, 16 * mt, m, row0, (int64_t)blockIdx.x * 32, a.I, a.h, a.h_scale);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int lr = 16 * mt + 4 * g + v;
+        if (lr < m) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const int64_t n = (int64_t)blockIdx.x * 64 + 16 * f + r16;
+            if (fvalid[f]) store_out<kYBF16>(a.out, (row0 + lr) * a.N + n, tot[f][v]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool kActFP4, int kMode, bool kYBF16>
+static void launch_stream_mt(const GemmArgs& a, int mt, dim3 grid, hipStream_t stream) {
+  switch (mt) {
+    case 1: gemm_stream_kernel<kActFP4, kMode, kYBF16, 1><<<grid, 256, 0, stream>>>(a); break;
+    case 2: gemm_stream_kernel<kActFP4, kMode, kYBF16, 2><<<grid, 256, 0, stream>>>(a); break;
+    case 3: gemm_stream_kernel<kActFP4, kMode, kYBF16, 3><<<grid, 256, 0, stream>>>(a); break;
+    default: gemm_stream_kernel<kActFP4, kMode, kYBF16, 4><<<grid, 256, 0, stream>>>(a); break;
+  }
+}
+
+template <bool kActFP4>
+static void launch_stream_fmt(int mode, bool y_bf16, const GemmArgs& a, int mt, dim3 grid, hipStream_t stream) {
+  if (mode == kModeFC1) launch_stream_mt<kActFP4, kModeFC1, false>(a, mt, grid, stream);
+  else if (mode == kModeDense) launch_stream_mt<kActFP4, kModeDense, false>(a, mt, grid, stream);
+  else if (y_bf16) launch_stream_mt<kActFP4, kModeFC2, true>(a, mt, grid, stream);
+  else launch_stream_mt<kActFP4, kModeFC2, false>(a, mt, grid, stream);
+}
+
+void launch_stream_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int mt, dim3 grid,
+                        hipStream_t stream) {
+  if (act_fp4) launch_stream_fmt<true>(mode, y_bf16, a, mt, grid, stream);
+  else launch_stream_fmt<false>(mode, y_bf16, a, mt, grid, stream);
+}
+
+}  // namespace mxf

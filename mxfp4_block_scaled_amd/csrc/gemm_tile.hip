@@ -1,0 +1,366 @@
+// LDS-ring MXFP4 GEMM for many rows per expert (prefill, dense M > 64) on the
+// 32x32x64 scaled MFMA.
+#include "gemm_common.hpp"
+
+namespace mxf {
+
+// ---------------------------------------------------------------------------------
+// LDS-ring kernel, 32x32x64 scaled MFMA: 128 rows x 256 weight rows per workgroup
+// (4 waves of 64 x 128). Operand tiles go HBM -> LDS with global_load_lds_dwordx4
+// (no staging registers) into a ring of NS stage slots; the loads of stage st+NS-1
+// are issued while stage st is computed, so NS-1 stages are in flight. Each slot is
+// its own __shared__ object so the compiler can tell the slot being read from the
+// slots being filled; lds_barrier() keeps the loads in flight across the barrier
+// and an explicit vmcnt wait (counted in load instructions per wave) marks a
+// stage as landed. 16-byte chunks are XOR-swizzled within a row: a lane of a DMA
+// instruction writes LDS chunk p (fixed by its lane id) and fetches the global
+// chunk that belongs there.
+namespace t3 {
+constexpr int BM = tile::BM, BN = tile::BN;
+}  // namespace t3
+
+template <bool kActFP4>
+struct T3Cfg {
+  static constexpr int KS = 256;                    // k per stage
+  static constexpr int NS = kActFP4 ? 3 : 2;        // ring slots (a 3rd FP8 slot would not fit in LDS)
+  static constexpr int S = KS / 64;                 // MFMA steps per stage
+  static constexpr int RA = kActFP4 ? KS / 2 : KS;  // A bytes per row per stage
+  static constexpr int RB = KS / 2;                 // B bytes per row per stage
+  static constexpr int CA = RA / 16, CB = RB / 16;  // 16-byte chunks per row
+  static constexpr int SB = KS / 32;                // scale bytes per row per stage
+  static constexpr int IA = t3::BM * CA / 64 / 4;   // A DMA instructions per wave
+  static constexpr int IB = t3::BN * CB / 64 / 4;   // B DMA instructions per wave
+  static constexpr int ISA = t3::BM * SB / 256 / 4; // A-scale DMA instructions (4 B per lane) per wave
+  static constexpr int ISB = t3::BN * SB / 256 / 4; // B-scale DMA instructions per wave
+  static constexpr int D = IA + IB + ISA + ISB;      // DMA instructions per wave per stage
+};
+
+template <bool kActFP4>
+struct alignas(16) T3Slot {
+  uint8_t A[t3::BM * T3Cfg<kActFP4>::RA];
+  uint8_t B[t3::BN * T3Cfg<kActFP4>::RB];
+  uint8_t As[t3::BM * T3Cfg<kActFP4>::SB];
+  uint8_t Bs[t3::BN * T3Cfg<kActFP4>::SB];
+};
+
+// NST > 0: the stage count K / 256 is a compile-time constant and the ring loop is
+// fully unrolled (a runtime loop makes the compiler drain all loads once per ring
+// turn); NST == 0: any K (multiple of 256) with a runtime loop.
+template <bool kActFP4, int kMode, bool kYBF16, int NST>
+__global__ void __launch_bounds__(256) gemm_tile3_kernel(GemmArgs a) {
+  using namespace t3;
+  using C = T3Cfg<kActFP4>;
+  constexpr int kFA = kActFP4 ? kFmtFP4 : kFmtFP8;
+  struct alignas(16) NoSlot {
+    uint8_t pad[16];
+  };
+  __shared__ T3Slot<kActFP4> slot0, slot1;
+  __shared__ typename std::conditional<kActFP4, T3Slot<kActFP4>, NoSlot>::type slot2;  // 3rd slot: FP4 only
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // XCD-aware order (block b runs on XCD b % 8): XCD x owns n-tiles [x*nt/8, (x+1)*nt/8)
+  const int ntiles = a.ntiles;
+  const int x = (int)(blockIdx.x & 7u), jb = (int)(blockIdx.x >> 3);
+  const int n_lo = x * ntiles / 8, n_hi = (x + 1) * ntiles / 8, nn = n_hi - n_lo;
+  if (nn == 0) return;
+  const int m_unit = jb / nn;
+  const int n_tile = n_lo + jb % nn;
+
+  int e = 0;
+  int64_t row0;
+  int m;
+  if (kMode == kModeDense) {
+    row0 = (int64_t)m_unit * BM;
+    if (row0 >= a.M) return;
+    m = (int)(a.M - row0 < BM ? a.M - row0 : BM);
+  } else {
+    int loc;
+    find_unit<BM>(a.offsets, a.E, m_unit, e, loc);
+    if (e < 0) return;
+    row0 = a.offsets[e] + (int64_t)loc * BM;
+    m = min(BM, a.offsets[e + 1] - (int)row0);
+  }
+  const int64_t K = a.K;
+  const int64_t wrow = K / 2, srow = K / 32;
+  const int64_t arow = kActFP4 ? K / 2 : K;
+
+  // activation row (rows past m read row 0 of the tile's first source; never stored)
+  auto a_src_row = [&](int r) -> int64_t {
+    if (r >= m) r = 0;
+    return (kMode == kModeFC1) ? (int64_t)(a.sorted_pair[row0 + r] / a.topk) : row0 + r;
+  };
+  auto b_row = [&](int r) -> int64_t {
+    if (kMode == kModeFC1) return (r < BN / 2 ? 0 : a.I - BN / 2) + (int64_t)n_tile * (BN / 2) + r;
+    return (int64_t)n_tile * BN + r;
+  };
+
+  // per-lane global sources of this wave's DMA instructions (stage 0)
+  const uint8_t* pa[C::IA];
+  const uint8_t* pb[C::IB];
+  const uint8_t* psa[C::ISA];
+  const uint8_t* psb[C::ISB];
+#pragma unroll
+  for (int q = 0; q < C::IA; ++q) {
+    const int chunk = (wave * C::IA + q) * 64 + lane;  // LDS chunk this lane fills
+    const int r = chunk / C::CA, pc = chunk % C::CA;
+    pa[q] = a.act + a_src_row(r) * arow + 16 * (pc ^ swz<C::CA>(r));
+  }
+#pragma unroll
+  for (int q = 0; q < C::IB; ++q) {
+    const int chunk = (wave * C::IB + q) * 64 + lane;
+    const int r = chunk / C::CB, pc = chunk % C::CB;
+    pb[q] = a.w + ((int64_t)e * a.N + b_row(r)) * wrow + 16 * (pc ^ swz<C::CB>(r));
+  }
+#pragma unroll
+  for (int q = 0; q < C::ISA; ++q) {
+    const int dw = (wave * C::ISA + q) * 64 + lane;  // dword of the A-scale slot
+    const int r = dw / (C::SB / 4), part = dw % (C::SB / 4);
+    psa[q] = a.act_scale + a_src_row(r) * srow + 4 * part;
+  }
+#pragma unroll
+  for (int q = 0; q < C::ISB; ++q) {
+    const int dw = (wave * C::ISB + q) * 64 + lane;
+    const int r = dw / (C::SB / 4), part = dw % (C::SB / 4);
+    psb[q] = a.w_scale + ((int64_t)e * a.N + b_row(r)) * srow + 4 * part;
+  }
+
+  auto issue = [&](T3Slot<kActFP4>& sl, int st) {
+    const int64_t oa = (int64_t)st * C::RA, ob = (int64_t)st * C::RB, os = (int64_t)st * C::SB;
+#pragma unroll
+    for (int q = 0; q < C::IA; ++q)
+      dma16_to_lds(pa[q] + oa, &sl.A[(wave * C::IA + q) * 1024]);
+#pragma unroll
+    for (int q = 0; q < C::IB; ++q)
+      dma16_to_lds(pb[q] + ob, &sl.B[(wave * C::IB + q) * 1024]);
+#pragma unroll
+    for (int q = 0; q < C::ISA; ++q)
+      dma4_to_lds(psa[q] + os, &sl.As[(wave * C::ISA + q) * 256]);
+#pragma unroll
+    for (int q = 0; q < C::ISB; ++q)
+      dma4_to_lds(psb[q] + os, &sl.Bs[(wave * C::ISB + q) * 256]);
+  };
+
+  v16f acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[i][q] = v16f{};
+
+  int arow_l[2], brow_l[4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) arow_l[f] = 64 * wm + 32 * f + r32;
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    if (kMode == kModeFC1) brow_l[f] = (f < 2 ? 0 : BN / 2) + 64 * wn + 32 * (f & 1) + r32;
+    else brow_l[f] = 128 * wn + 32 * f + r32;
+  }
+
+  auto compute = [&](const T3Slot<kActFP4>& sl) {
+    int sa[2], sb[4];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      if (C::SB == 8) sa[f] = *reinterpret_cast<const int*>(&sl.As[arow_l[f] * 8 + 4 * g]);
+      else sa[f] = *reinterpret_cast<const uint16_t*>(&sl.As[arow_l[f] * 4 + 2 * g]);
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if (C::SB == 8) sb[f] = *reinterpret_cast<const int*>(&sl.Bs[brow_l[f] * 8 + 4 * g]);
+      else sb[f] = *reinterpret_cast<const uint16_t*>(&sl.Bs[brow_l[f] * 4 + 2 * g]);
+    }
+#pragma unroll
+    for (int s = 0; s < C::S; ++s) {
+      v8i af[2], bf[4];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int r = arow_l[f];
+        const uint8_t* rowp = &sl.A[r * C::RA];
+        if (kActFP4) {
+          const int c = C::S * g + s;
+          const v4i x4 = *reinterpret_cast<const v4i*>(rowp + 16 * (c ^ swz<C::CA>(r)));
+          af[f] = v8i{x4[0], x4[1], x4[2], x4[3], 0, 0, 0, 0};
+        } else {
+          const int c1 = 2 * s + g, c2 = 2 * (C::S + s) + g;
+          const v4i lo = *reinterpret_cast<const v4i*>(rowp + 16 * (c1 ^ swz<C::CA>(r)));
+          const v4i hi = *reinterpret_cast<const v4i*>(rowp + 16 * (c2 ^ swz<C::CA>(r)));
+          af[f] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+      }
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int r = brow_l[f];
+        const int c = C::S * g + s;
+        const v4i y4 = *reinterpret_cast<const v4i*>(&sl.B[r * C::RB + 16 * (c ^ swz<C::CB>(r))]);
+        bf[f] = v8i{y4[0], y4[1], y4[2], y4[3], 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn) {
+          if (s == 0) acc[fm][fn] = mfma32x32x64<kFA, kFmtFP4, 0>(af[fm], bf[fn], acc[fm][fn], sa[fm], sb[fn]);
+          else if (s == 1) acc[fm][fn] = mfma32x32x64<kFA, kFmtFP4, 1>(af[fm], bf[fn], acc[fm][fn], sa[fm], sb[fn]);
+          else if (s == 2) acc[fm][fn] = mfma32x32x64<kFA, kFmtFP4, 2>(af[fm], bf[fn], acc[fm][fn], sa[fm], sb[fn]);
+          else acc[fm][fn] = mfma32x32x64<kFA, kFmtFP4, 3>(af[fm], bf[fn], acc[fm][fn], sa[fm], sb[fn]);
+        }
+    }
+  };
+
+  // ring pipeline: at stage st, stages st..st+NS-2 have been issued; wait for st
+  // (leaving the later ones in flight), barrier, refill the slot freed by st-1, compute st
+  constexpr int NS = C::NS, D = C::D;
+  const int nst = NST > 0 ? NST : (int)(K / C::KS);
+  // every ring step is a compile-time instance, so each DMA and each LDS read names
+  // its slot object (the compiler then keeps the loads of other slots in flight)
+  auto slot_of = [&](auto I) -> T3Slot<kActFP4>& {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) {
+      return slot0;
+    } else if constexpr (i == 1) {
+      return slot1;
+    } else {
+      if constexpr (kActFP4) return slot2;  // the 3rd slot exists for FP4 only
+      else return slot0;                    // never reached: FP8 runs a 2-slot ring
+    }
+  };
+  auto step = [&](auto I, int st) {
+    constexpr int i = decltype(I)::value;
+    constexpr int inext = (i + NS - 1) % NS;
+    if (NS == 3 && st + 1 < nst) wait_vmcnt<D>();  // stage st+1 may stay in flight
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (st + NS - 1 < nst) issue(slot_of(std::integral_constant<int, inext>{}), st + NS - 1);
+    compute(slot_of(I));
+  };
+  issue(slot0, 0);
+  if constexpr (NS == 3) {
+    if (nst > 1) issue(slot1, 1);
+  }
+  auto ring_turn = [&](int st0) {
+    step(std::integral_constant<int, 0>{}, st0);
+    if (st0 + 1 < nst) step(std::integral_constant<int, 1>{}, st0 + 1);
+    if constexpr (NS == 3) {
+      if (st0 + 2 < nst) step(std::integral_constant<int, 2>{}, st0 + 2);
+    }
+  };
+  if constexpr (NST > 0) {
+#pragma unroll
+    for (int st0 = 0; st0 < NST; st0 += NS) ring_turn(st0);
+  } else {
+    for (int st0 = 0; st0 < nst; st0 += NS) ring_turn(st0);
+  }
+  lds_barrier();  // every wave is done reading the ring; slot0 becomes epilogue staging
+
+  // epilogues, 64-row halves staged in slot0 (the waves with wm == half write)
+  uint8_t* stage = slot0.A;
+  if (kMode == kModeFC1) {
+    float(*hf)[BN / 2 + 4] = reinterpret_cast<float(*)[BN / 2 + 4]>(stage);
+    const int64_t i0 = (int64_t)n_tile * (BN / 2);
+    const int64_t hrow = kActFP4 ? a.I / 2 : a.I;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int rr = 32 * fm + 8 * (v >> 2) + 4 * g + (v & 3);
+              hf[rr][64 * wn + 32 * f + r32] = silu_mul(acc[fm][f][v], acc[fm][f + 2][v]);
+            }
+      }
+      __syncthreads();
+      const int rr = tid >> 2, blk = tid & 3;  // 64 rows x 4 blocks of 32 = 256 items
+      const int lr = 64 * half + rr;
+      if (lr < m) {
+        const int64_t R = row0 + lr;
+        quantize_store32<kActFP4>(&hf[rr][32 * blk], a.h + R * hrow + (i0 + 32 * blk) / (kActFP4 ? 2 : 1),
+                                  a.h_scale + R * (a.I / 32) + i0 / 32 + blk);
+      }
+      __syncthreads();
+    }
+  } else if (kYBF16) {
+    uint16_t(*ob)[BN + 8] = reinterpret_cast<uint16_t(*)[BN + 8]>(stage);
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int rr = 32 * fm + 8 * (v >> 2) + 4 * g + (v & 3);
+              ob[rr][128 * wn + 32 * fn + r32] = (uint16_t)bf16_round(acc[fm][fn][v]);
+            }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < (64 * BN / 8) / 256; ++q) {
+        const int idx = tid + 256 * q;
+        const int rr = idx >> 5, cc = (idx & 31) * 8;
+        const int lr = 64 * half + rr;
+        if (lr < m)
+          *reinterpret_cast<uint4*>(out + (row0 + lr) * a.N + (int64_t)n_tile * BN + cc) =
+              *reinterpret_cast<const uint4*>(&ob[rr][cc]);
+      }
+      __syncthreads();
+    }
+  } else {
+    float(*of)[BN + 4] = reinterpret_cast<float(*)[BN + 4]>(stage);
+    float* out = static_cast<float*>(a.out);
+#pragma unroll
+    for (int quarter = 0; quarter < 4; ++quarter) {
+      if (wm == (quarter >> 1)) {
+        const int fm = quarter & 1;
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rr = 8 * (v >> 2) + 4 * g + (v & 3);
+            of[rr][128 * wn + 32 * fn + r32] = acc[fm][fn][v];
+          }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < (32 * BN / 4) / 256; ++q) {
+        const int idx = tid + 256 * q;
+        const int rr = idx >> 6, cc = (idx & 63) * 4;
+        const int lr = 32 * quarter + rr;
+        if (lr < m)
+          *reinterpret_cast<float4*>(out + (row0 + lr) * a.N + (int64_t)n_tile * BN + cc) =
+              *reinterpret_cast<const float4*>(&of[rr][cc]);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <bool kActFP4, int kMode, bool kYBF16>
+static void launch_tile3(const GemmArgs& a, int64_t m_units, hipStream_t stream) {
+  const int64_t nn3 = cdiv(a.ntiles, 8);
+  const dim3 g3((unsigned)(8 * nn3 * m_units));
+  // fully unrolled instances for K = 7168 and K = 2048 (the layer's H and I)
+  const int64_t nst = a.K / 256;
+  if (nst == 28) gemm_tile3_kernel<kActFP4, kMode, kYBF16, 28><<<g3, 256, 0, stream>>>(a);
+  else if (nst == 8) gemm_tile3_kernel<kActFP4, kMode, kYBF16, 8><<<g3, 256, 0, stream>>>(a);
+  else gemm_tile3_kernel<kActFP4, kMode, kYBF16, 0><<<g3, 256, 0, stream>>>(a);
+}
+
+template <bool kActFP4>
+static void launch_tile_fmt(int mode, bool y_bf16, const GemmArgs& a, int64_t m_units, hipStream_t stream) {
+  if (mode == kModeFC1) launch_tile3<kActFP4, kModeFC1, false>(a, m_units, stream);
+  else if (mode == kModeDense) launch_tile3<kActFP4, kModeDense, false>(a, m_units, stream);
+  else if (y_bf16) launch_tile3<kActFP4, kModeFC2, true>(a, m_units, stream);
+  else launch_tile3<kActFP4, kModeFC2, false>(a, m_units, stream);
+}
+
+void launch_tile_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int64_t m_units,
+                      hipStream_t stream) {
+  if (act_fp4) launch_tile_fmt<true>(mode, y_bf16, a, m_units, stream);
+  else launch_tile_fmt<false>(mode, y_bf16, a, m_units, stream);
+}
+
+}  // namespace mxf
