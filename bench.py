@@ -41,18 +41,27 @@ BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,
 
 # HBM bytes per grouped-GEMM call (FC1 + FC2 launches) from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # passes, scaled by a 1 GiB copy (2.0 x FETCH_SIZE + 1.0 x WRITE_SIZE; the passes and the
-# calibration are in profiles/moe_layer_hbm_traffic.md). They hold only for the GEMM source
-# they were measured on: on any other source the roofline reports traffic = null.
+# calibration are in profiles/moe_layer_hbm_traffic.md). They hold only for the GEMM sources
+# they were measured on (sha-256 over GEMM_SOURCES): on any other source traffic = null.
 TRAFFIC_SRC_SHA256 = "123f63900cb781546edffd7c1c0063debe44c5e96bd57712476ed576aca57969"
 TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 12361979904, "moe_decode_t8": 1030335488}
 
 
-def measured_traffic(workload):
+GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip")
+
+
+def gemm_sources_sha256():
     import hashlib
-    src = os.path.join(ROOT, "mxfp4_block_scaled_amd", "csrc", "gemm.hip")
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != TRAFFIC_SRC_SHA256:
-            return None
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "mxfp4_block_scaled_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    if gemm_sources_sha256() != TRAFFIC_SRC_SHA256:
+        return None
     return TRAFFIC_BYTES.get(workload)
 
 

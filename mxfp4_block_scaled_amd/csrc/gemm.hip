@@ -20,6 +20,7 @@ int launch_dense_gemm(const uint8_t* qa, const uint8_t* qa_scale, bool act_fp4, 
     a.act_scale = qa_scale;
     a.out = c;
     a.M = M;
+    a.act_rows = M;
     a.ntiles = (int)(N / tile::BN);
     launch_tile_gemm(kModeDense, false, act_fp4, a, cdiv(M, tile::BM), stream);
   } else {
@@ -43,6 +44,7 @@ int launch_grouped_gemm(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, 
   if (R == 0) return 0;
   GemmArgs f1{};
   f1.act = q;
+  f1.act_rows = T;
   f1.act_scale = q_scale;
   f1.w = w1;
   f1.w_scale = w1_scale;
@@ -57,6 +59,7 @@ int launch_grouped_gemm(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, 
   f1.E = E;
   GemmArgs f2 = f1;
   f2.act = h;
+  f2.act_rows = R;
   f2.act_scale = h_scale;
   f2.w = w2;
   f2.w_scale = w2_scale;

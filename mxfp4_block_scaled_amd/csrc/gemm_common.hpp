@@ -31,6 +31,7 @@ struct GemmArgs {
   uint8_t* h_scale;          // FC1 out [R][I/32]
   void* out;                 // FC2: y [R][N]; dense: c [M][N]
   int64_t K, N, I, M;
+  int64_t act_rows;  // rows of act / act_scale (FC1: T, FC2: T * topk, dense: M)
   int topk, E;
   int ntiles;  // tile kernel: weight-row tiles per expert (1-D grid: block = m_unit * ntiles + n_tile)
 };
@@ -160,6 +161,53 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+#endif
+}
+
+// Raw buffer resources (base, byte size): loads through them are range-checked
+// by the hardware (out-of-range lanes read zero), and their HBM -> LDS form is a
+// MUBUF instruction, which the compiler's wait-count tracking keeps apart from
+// the plain register loads it can then wait for precisely.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+#else
+struct buf_rsrc {
+  int w[4];
+};
+#endif
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // dword 3 = 0x00020000: raw (untyped) 32-bit data format on gfx9-family parts
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+#else
+  (void)base;
+  (void)bytes;
+  return buf_rsrc{};
+#endif
+}
+// 16 (or 4) bytes per lane from byte offset voff + soff to lds + 16 lane (4 lane)
+__device__ __forceinline__ void buf_dma16(buf_rsrc r, void* lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, (int)soff, 0, 0);
+#endif
+}
+__device__ __forceinline__ void buf_dma4(buf_rsrc r, void* lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, (int)voff, (int)soff, 0, 0);
+#endif
+}
+__device__ __forceinline__ v4i buf_load16(buf_rsrc r, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+#else
+  return v4i{};
+#endif
+}
+__device__ __forceinline__ int buf_load4(buf_rsrc r, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+#else
+  return 0;
 #endif
 }
 
