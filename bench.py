@@ -192,7 +192,7 @@ def bench_dense(steps, warmup, rotate=48):
     sets = [(w0, s0)] + [(w0.clone(), s0.clone()) for _ in range(rotate - 1)]
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     lib = ops.load()
-    ws = torch.empty(lib.mxfp4_gemm_workspace_bytes(M, K, 0), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(lib.mxfp4_gemm_workspace_bytes(M, N, K, 0), dtype=torch.uint8, device="cuda")
     c = torch.empty((M, N), dtype=torch.float32, device="cuda")
     it = [0]
 

@@ -69,7 +69,7 @@ const char* mxf_status_str(int status);
 
 /* ABI version of this header (bumped on any signature change). */
 int mxf_abi_version(void);
-#define MXF_ABI_VERSION 1
+#define MXF_ABI_VERSION 2
 
 /*
  * mxfp4_quantize_act - quantise activation rows per 32-element block.
@@ -91,13 +91,16 @@ int mxfp4_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t K, int 
  *   w        [N][K/2] E2M1 codes, w_scale [N][K/32] UE8M0
  *   c        [M][N] fp32 output (fp32 accumulation of exact products)
  *   workspace, workspace_bytes: device scratch of at least
- *            mxfp4_gemm_workspace_bytes(M, K, act_fmt) bytes (16-byte aligned);
- *            its contents on entry are ignored and on exit undefined.
+ *            mxfp4_gemm_workspace_bytes(M, N, K, act_fmt) bytes (16-byte
+ *            aligned): the quantised activations and, for M <= 64, the fp32
+ *            partial sums of the K slices; its contents on entry are ignored and
+ *            on exit undefined. The slice sums are added in a fixed order, so
+ *            results are bit-identical from run to run.
  * Requires K % 512 == 0 (one 512-k super-step of scaled-MFMA K steps) and
  * N % 16 == 0; M >= 0 (M == 0 is a no-op).
  * Errors: NULL, SHAPE, ALIGN, FORMAT, WORKSPACE.
  */
-size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t K, int act_fmt);
+size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_fmt);
 int mxfp4_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K, int act_fmt,
                const uint8_t* w, const uint8_t* w_scale, float* c,
                void* workspace, size_t workspace_bytes, mxf_stream stream);

@@ -51,10 +51,12 @@ int mxfp4_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t K, int 
   return rc ? MXF_ERR_LAUNCH : MXF_OK;
 }
 
-size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t K, int act_fmt) {
-  if (M <= 0 || K <= 0) return 0;
+size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_fmt) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
   const size_t codes = (size_t)M * (size_t)(act_fmt == MXF_E2M1 ? K / 2 : K);
-  return round_up(codes, 256) + round_up((size_t)M * (size_t)(K / 32), 256);
+  const int S = mxf::dense_ksplit(M, N, K);
+  const size_t partials = S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+  return round_up(codes, 256) + round_up((size_t)M * (size_t)(K / 32), 256) + round_up(partials, 256);
 }
 
 int mxfp4_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K, int act_fmt, const uint8_t* w,
@@ -64,15 +66,16 @@ int mxfp4_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K, int act_fmt, 
   if (M == 0) return MXF_OK;
   if (!a || !w || !w_scale || !c) return MXF_ERR_NULL;
   if (!aligned16(a) || !aligned16(w) || !aligned16(w_scale) || !aligned16(c)) return MXF_ERR_ALIGN;
-  const size_t need = mxfp4_gemm_workspace_bytes(M, K, act_fmt);
+  const size_t need = mxfp4_gemm_workspace_bytes(M, N, K, act_fmt);
   if (!workspace || workspace_bytes < need) return MXF_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MXF_ERR_ALIGN;
   uint8_t* qa = static_cast<uint8_t*>(workspace);
   uint8_t* qs = qa + round_up((size_t)M * (size_t)(act_fmt == MXF_E2M1 ? K / 2 : K), 256);
+  float* part = reinterpret_cast<float*>(qs + round_up((size_t)M * (size_t)(K / 32), 256));
   const bool fp4 = act_fmt == MXF_E2M1;
   hipStream_t s = as_stream(stream);
   if (mxf::launch_quantize_act(a, false, M, K, fp4, qa, qs, s)) return MXF_ERR_LAUNCH;
-  if (mxf::launch_dense_gemm(qa, qs, fp4, M, N, K, w, w_scale, c, s)) return MXF_ERR_LAUNCH;
+  if (mxf::launch_dense_gemm(qa, qs, fp4, M, N, K, w, w_scale, c, part, s)) return MXF_ERR_LAUNCH;
   return MXF_OK;
 }
 

@@ -4,8 +4,17 @@
 
 namespace mxf {
 
+int dense_ksplit(int64_t M, int64_t N, int64_t K) {
+  // M <= 64 streams the weights with 64 weight rows per workgroup: N / 64 workgroups
+  // fill the chip only for very wide N, so K is also split into slices of 4
+  // super-steps (one per wave), summed afterwards in a fixed order
+  if (M <= 0 || M > 64 || N % 4 != 0) return 1;
+  const int64_t nss = K / 512;
+  return (int)(nss > 4 ? cdiv(nss, 4) : 1);
+}
+
 int launch_dense_gemm(const uint8_t* qa, const uint8_t* qa_scale, bool act_fp4, int64_t M, int64_t N, int64_t K,
-                      const uint8_t* w, const uint8_t* w_scale, float* c, hipStream_t stream) {
+                      const uint8_t* w, const uint8_t* w_scale, float* c, float* partials, hipStream_t stream) {
   if (M == 0) return 0;
   GemmArgs a{};
   a.w = w;
@@ -23,6 +32,15 @@ int launch_dense_gemm(const uint8_t* qa, const uint8_t* qa_scale, bool act_fp4, 
     a.act_rows = M;
     a.ntiles = (int)(N / tile::BN);
     launch_tile_gemm(kModeDense, false, act_fp4, a, cdiv(M, tile::BM), stream);
+  } else if (dense_ksplit(M, N, K) > 1) {
+    const int S = dense_ksplit(M, N, K);
+    a.act = qa;
+    a.act_scale = qa_scale;
+    a.out = partials;
+    a.M = M;
+    a.kchunk = 4;
+    launch_stream_gemm(kModeDense, false, act_fp4, a, (int)cdiv(M, 16), dim3((unsigned)cdiv(N, 64), (unsigned)S), stream);
+    launch_reduce_partials(partials, S, M * N, c, stream);
   } else {
     for (int64_t m0 = 0; m0 < M; m0 += 64) {
       const int64_t mm = M - m0 < 64 ? M - m0 : 64;

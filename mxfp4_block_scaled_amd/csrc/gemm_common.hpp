@@ -34,6 +34,7 @@ struct GemmArgs {
   int64_t act_rows;  // rows of act / act_scale (FC1: T, FC2: T * topk, dense: M)
   int topk, E;
   int ntiles;  // tile kernel: weight-row tiles per expert (1-D grid: block = m_unit * ntiles + n_tile)
+  int kchunk;  // dense weight-streaming kernel: 512-k super-steps per grid.y slice (0: the whole K)
 };
 
 // ---------------------------------------------------------------------------------
@@ -215,6 +216,9 @@ __device__ __forceinline__ int buf_load4(buf_rsrc r, uint32_t voff, uint32_t sof
 namespace tile {
 constexpr int BM = 128, BN = 256;
 }  // namespace tile
+
+// c[i] = sum over s < S of part[s * n + i], in the order s = 0 .. S-1 (n % 4 == 0)
+void launch_reduce_partials(const float* part, int S, int64_t n, float* c, hipStream_t stream);
 
 // kernel launchers (gemm_stream.hip, gemm_tile.hip); mode is kModeFC1 / kModeFC2 / kModeDense
 void launch_stream_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int mt, dim3 grid,

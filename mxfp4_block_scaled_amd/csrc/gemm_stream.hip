@@ -128,8 +128,16 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[mt][f] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // dense with kchunk > 0: grid.y slice s covers super-steps [s kchunk, (s+1) kchunk)
+  // and writes its partial sums to slice s of out ([grid.y][M][N])
   const int nss = (int)(K / 512);
-  const int ss_begin = wave * nss / 4, ss_end = (wave + 1) * nss / 4;
+  int ss_lo = 0, ss_hi = nss;
+  if (kMode == kModeDense && a.kchunk > 0) {
+    ss_lo = (int)blockIdx.y * a.kchunk;
+    ss_hi = min(nss, ss_lo + a.kchunk);
+  }
+  const int len = ss_hi - ss_lo;
+  const int ss_begin = ss_lo + wave * len / 4, ss_end = ss_lo + (wave + 1) * len / 4;
   for (int ss = ss_begin; ss < ss_end; ++ss) {
     v4i bq[4][4];
     int bs[4];
@@ -186,6 +194,9 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
     }
   }
 
+  void* const out = kMode == kModeDense && a.kchunk > 0
+                        ? static_cast<void*>(static_cast<float*>(a.out) + (int64_t)blockIdx.y * a.M * a.N)
+                        : a.out;
   // reduce the 4 K-slices in a fixed order (deterministic)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -213,7 +224,7 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
           for (int f = 0; f < 4; ++f) {
             const int64_t n = (int64_t)blockIdx.x * 64 + 16 * f + r16;
-            if (fvalid[f]) store_out<kYBF16>(a.out, (row0 + lr) * a.N + n, tot[f][v]);
+            if (fvalid[f]) store_out<kYBF16>(out, (row0 + lr) * a.N + n, tot[f][v]);
           }
         }
       }
@@ -237,6 +248,27 @@ static void launch_stream_fmt(int mode, bool y_bf16, const GemmArgs& a, int mt, 
   else if (mode == kModeDense) launch_stream_mt<kActFP4, kModeDense, false>(a, mt, grid, stream);
   else if (y_bf16) launch_stream_mt<kActFP4, kModeFC2, true>(a, mt, grid, stream);
   else launch_stream_mt<kActFP4, kModeFC2, false>(a, mt, grid, stream);
+}
+
+__global__ void __launch_bounds__(256) reduce_partials_kernel(const float4* __restrict__ part, int S, int64_t n4,
+                                                              float4* __restrict__ c) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 acc = part[i];
+  for (int s = 1; s < S; ++s) {
+    const float4 p = part[(int64_t)s * n4 + i];
+    acc.x += p.x;
+    acc.y += p.y;
+    acc.z += p.z;
+    acc.w += p.w;
+  }
+  c[i] = acc;
+}
+
+void launch_reduce_partials(const float* part, int S, int64_t n, float* c, hipStream_t stream) {
+  const int64_t n4 = n / 4;
+  reduce_partials_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, stream>>>(reinterpret_cast<const float4*>(part), S, n4,
+                                                                     reinterpret_cast<float4*>(c));
 }
 
 void launch_stream_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int mt, dim3 grid,

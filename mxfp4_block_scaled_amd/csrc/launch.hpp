@@ -21,9 +21,14 @@ int launch_route_permute(const float* logits, int64_t T, int E, int topk, int32_
 int launch_combine(const void* y, bool y_bf16, const float* gates, const int32_t* pair_row,
                    int64_t T, int topk, int64_t H, void* out, bool out_bf16, hipStream_t stream);
 
-// dense C[M][N] (fp32) = A_hat (already quantised, [M][K] codes + scales) x W_hat^T
+// number of K slices the dense GEMM splits into (1: none); with more than one it
+// needs dense_ksplit * M * N fp32 of partial sums
+int dense_ksplit(int64_t M, int64_t N, int64_t K);
+
+// dense C[M][N] (fp32) = A_hat (already quantised, [M][K] codes + scales) x W_hat^T;
+// partials: dense_ksplit(M, N, K) * M * N fp32 of scratch when that is above 1
 int launch_dense_gemm(const uint8_t* qa, const uint8_t* qa_scale, bool act_fp4, int64_t M, int64_t N,
-                      int64_t K, const uint8_t* w, const uint8_t* w_scale, float* c,
+                      int64_t K, const uint8_t* w, const uint8_t* w_scale, float* c, float* partials,
                       hipStream_t stream);
 
 int launch_grouped_gemm(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, int64_t T, int topk,

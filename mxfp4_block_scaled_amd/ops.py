@@ -25,7 +25,7 @@ SIGNATURES = {
     "mxf_status_str": (ctypes.c_char_p, [_c_int]),
     "mxf_abi_version": (_c_int, []),
     "mxfp4_quantize_act": (_c_int, [_p, _c_int, _c_i64, _c_i64, _c_int, _p, _p, _p]),
-    "mxfp4_gemm_workspace_bytes": (_sz, [_c_i64, _c_i64, _c_int]),
+    "mxfp4_gemm_workspace_bytes": (_sz, [_c_i64, _c_i64, _c_i64, _c_int]),
     "mxfp4_gemm": (_c_int, [_p, _c_i64, _c_i64, _c_i64, _c_int, _p, _p, _p, _p, _sz, _p]),
     "moe_route_permute": (_c_int, [_p, _c_i64, _c_i32, _c_i32, _p, _p, _p, _p, _p, _p]),
     "moe_grouped_mxfp4_gemm": (_c_int, [_p, _p, _c_int, _c_i64, _c_i32, _c_i64, _c_i64, _c_i32,
@@ -96,7 +96,7 @@ def mxfp4_gemm(a, w, w_scale, act_fmt="e4m3", out=None, workspace=None):
     N = w.shape[0]
     f = FMTS[act_fmt]
     lib = load()
-    need = lib.mxfp4_gemm_workspace_bytes(M, K, f)
+    need = lib.mxfp4_gemm_workspace_bytes(M, N, K, f)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.mxf_abi_version() == 1
+    assert lib.mxf_abi_version() == 2
     for s in range(8):
         assert lib.mxf_status_str(s)
 
@@ -61,9 +61,14 @@ def test_quantize_errors():
 
 def test_gemm_errors():
     lib = _lib()
-    need = lib.mxfp4_gemm_workspace_bytes(16, 4096, 0)
-    assert need >= 16 * 4096 + 16 * 128
-    assert lib.mxfp4_gemm_workspace_bytes(16, 4096, 1) < need
+    need = lib.mxfp4_gemm_workspace_bytes(16, 32, 4096, 0)
+    # E4M3 codes + scale bytes + fp32 partial sums of the 2 K slices (8 super-steps of 512)
+    assert need >= 16 * 4096 + 16 * 128 + 2 * 16 * 32 * 4
+    assert lib.mxfp4_gemm_workspace_bytes(16, 32, 4096, 1) < need
+    # no K split above 64 rows, nor when K fits one slice of 4 super-steps
+    assert lib.mxfp4_gemm_workspace_bytes(100, 32, 4096, 0) < 100 * 4096 + 100 * 128 + 512
+    assert lib.mxfp4_gemm_workspace_bytes(16, 32, 2048, 0) < 16 * 2048 + 16 * 64 + 512
+    assert lib.mxfp4_gemm_workspace_bytes(0, 32, 4096, 0) == 0
     assert lib.mxfp4_gemm(A, 16, 32, 4096 + 64, 0, A, A, A, A, need, None) == SHAPE  # K % 512
     assert lib.mxfp4_gemm(A, 16, 40, 4096, 0, A, A, A, A, need, None) == SHAPE       # N % 16
     assert lib.mxfp4_gemm(A, 16, 32, 4096, 2, A, A, A, A, need, None) == FORMAT

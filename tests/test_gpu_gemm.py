@@ -29,8 +29,11 @@ def test_dense_workloads(name):
 
 @pytest.mark.parametrize("M,N,K,fmt", [
     (1, 16, 512, "e4m3"), (5, 48, 1024, "e4m3"), (17, 64, 2048, "e2m1"), (63, 80, 512, "e4m3"),
-    (70, 256, 1536, "e4m3"),  # M > 64 with N % 128 == 0 -> LDS-tiled kernel, ragged last tile
-    (300, 384, 1024, "e2m1"), (129, 96, 512, "e4m3"),  # M > 64, N % 128 != 0 -> streamed in 64-row chunks
+    (70, 256, 1536, "e4m3"),  # M > 64 with N % 256 == 0 -> LDS-tiled kernel, ragged last tile
+    (300, 384, 1024, "e2m1"), (129, 96, 512, "e4m3"),  # M > 64, N % 256 != 0 -> streamed in 64-row chunks
+    # M <= 64 with more than 4 super-steps of 512 k: K split into slices summed in a fixed order
+    (33, 48, 5120, "e2m1"),   # 3 slices, the last with 2 super-steps (two idle waves)
+    (64, 96, 2560, "e4m3"),   # 2 slices, the last with 1 super-step
 ])
 def test_dense_ragged_shapes(M, N, K, fmt):
     a = dg.activations(M * 7 + N, M, K, outliers=True)
