@@ -638,6 +638,276 @@ static void launch_tile4(const GemmArgs& a, int64_t m_units, hipStream_t stream)
 #define MXF_TILE4 1
 #endif
 
+// ---------------------------------------------------------------------------------
+// Eight-wave variant of the LDS-ring kernel: the same 128 x 256 tile, ring and
+// copies, computed by 8 waves of 64 x 64 (2 x 2 fragments) - two waves per SIMD,
+// so one wave's MFMAs run while the other waits at the barrier, on a copy or on
+// its LDS reads. FC1: wave (wm, wn) holds the gate rows of I-columns
+// [32 wn, 32 wn + 32) and the matching up rows; the epilogues stage through each
+// wave's own LDS region.
+template <bool kActFP4>
+struct T8Cfg {
+  using B = T3Cfg<kActFP4>;
+  static constexpr int IA = t3::BM * B::CA / 64 / 8;  // A copies per wave per stage (16 B per lane)
+  static constexpr int IB = t3::BN * B::CB / 64 / 8;  // B copies per wave per stage
+  static constexpr int D = IA + IB + 2;              // + one A-scale and one B-scale copy (4 B per lane)
+};
+
+template <bool kActFP4, int kMode, bool kYBF16, int NST>
+__global__ void __launch_bounds__(512) gemm_tile8_kernel(GemmArgs a) {
+  using namespace t3;
+  using C = T3Cfg<kActFP4>;
+  using C8 = T8Cfg<kActFP4>;
+  constexpr int kFA = kActFP4 ? kFmtFP4 : kFmtFP8;
+  struct alignas(16) NoSlot {
+    uint8_t pad[16];
+  };
+  __shared__ T3Slot<kActFP4> slot0, slot1;
+  __shared__ typename std::conditional<kActFP4, T3Slot<kActFP4>, NoSlot>::type slot2;  // 3rd slot: FP4 only
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  const int wm = wave >> 2, wn = wave & 3;
+
+  // XCD-aware order (block b runs on XCD b % 8): XCD x owns n-tiles [x*nt/8, (x+1)*nt/8)
+  const int ntiles = a.ntiles;
+  const int x = (int)(blockIdx.x & 7u), jb = (int)(blockIdx.x >> 3);
+  const int n_lo = x * ntiles / 8, n_hi = (x + 1) * ntiles / 8, nn = n_hi - n_lo;
+  if (nn == 0) return;
+  const int m_unit = jb / nn;
+  const int n_tile = n_lo + jb % nn;
+
+  int e = 0;
+  int64_t row0;
+  int m;
+  if (kMode == kModeDense) {
+    row0 = (int64_t)m_unit * BM;
+    if (row0 >= a.M) return;
+    m = (int)(a.M - row0 < BM ? a.M - row0 : BM);
+  } else {
+    int loc;
+    find_unit<BM>(a.offsets, a.E, m_unit, e, loc);
+    if (e < 0) return;
+    row0 = a.offsets[e] + (int64_t)loc * BM;
+    m = min(BM, a.offsets[e + 1] - (int)row0);
+  }
+  const int64_t K = a.K;
+  const int64_t wrow = K / 2, srow = K / 32;
+  const int64_t arow = kActFP4 ? K / 2 : K;
+
+  auto a_src_row = [&](int r) -> int64_t {  // rows past m read the tile's first row (never stored)
+    if (r >= m) r = 0;
+    return (kMode == kModeFC1) ? (int64_t)(a.sorted_pair[row0 + r] / a.topk) : row0 + r;
+  };
+  auto b_row = [&](int r) -> int64_t {
+    if (kMode == kModeFC1) return (r < BN / 2 ? 0 : a.I - BN / 2) + (int64_t)n_tile * (BN / 2) + r;
+    return (int64_t)n_tile * BN + r;
+  };
+
+  // per-lane copy sources of stage 0
+  const uint8_t* pa[C8::IA];
+  const uint8_t* pb[C8::IB];
+#pragma unroll
+  for (int q = 0; q < C8::IA; ++q) {
+    const int chunk = (wave * C8::IA + q) * 64 + lane;  // LDS chunk this lane fills
+    const int r = chunk / C::CA, pc = chunk % C::CA;
+    pa[q] = a.act + a_src_row(r) * arow + 16 * (pc ^ swz<C::CA>(r));
+  }
+#pragma unroll
+  for (int q = 0; q < C8::IB; ++q) {
+    const int chunk = (wave * C8::IB + q) * 64 + lane;
+    const int r = chunk / C::CB, pc = chunk % C::CB;
+    pb[q] = a.w + ((int64_t)e * a.N + b_row(r)) * wrow + 16 * (pc ^ swz<C::CB>(r));
+  }
+  // scale copies in 4-byte pieces (a copy writes lane l's piece at 4 l): the [128][8]
+  // A-scale slot by the first 32 lanes of each wave (wave w: rows 16 w .. 16 w + 15),
+  // the [256][8] B-scale slot by all 64 lanes (wave w: rows 32 w .. 32 w + 31)
+  const uint8_t* psa = a.act_scale + a_src_row(16 * wave + ((lane & 31) >> 1)) * srow + 4 * (lane & 1);
+  const uint8_t* psb = a.w_scale + ((int64_t)e * a.N + b_row(32 * wave + (lane >> 1))) * srow + 4 * (lane & 1);
+
+  auto issue = [&](T3Slot<kActFP4>& sl, int st) {
+    const int64_t oa = (int64_t)st * C::RA, ob = (int64_t)st * C::RB, os = (int64_t)st * C::SB;
+#pragma unroll
+    for (int q = 0; q < C8::IA; ++q) dma16_to_lds(pa[q] + oa, &sl.A[(wave * C8::IA + q) * 1024]);
+#pragma unroll
+    for (int q = 0; q < C8::IB; ++q) dma16_to_lds(pb[q] + ob, &sl.B[(wave * C8::IB + q) * 1024]);
+    if (lane < 32) dma4_to_lds(psa + os, &sl.As[wave * 128]);  // one instruction, half the lanes
+    dma4_to_lds(psb + os, &sl.Bs[wave * 256]);
+  };
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+  int arow_l[2], brow_l[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    arow_l[f] = 64 * wm + 32 * f + r32;
+    if (kMode == kModeFC1) brow_l[f] = (f == 0 ? 0 : BN / 2) + 32 * wn + r32;
+    else brow_l[f] = 64 * wn + 32 * f + r32;
+  }
+
+  auto compute = [&](const T3Slot<kActFP4>& sl) {
+    int sa[2], sb[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      sa[f] = *reinterpret_cast<const int*>(&sl.As[arow_l[f] * 8 + 4 * g]);
+      sb[f] = *reinterpret_cast<const int*>(&sl.Bs[brow_l[f] * 8 + 4 * g]);
+    }
+#pragma unroll
+    for (int s = 0; s < C::S; ++s) {
+      v8i af[2], bf[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int r = arow_l[f];
+        const uint8_t* rowp = &sl.A[r * C::RA];
+        if (kActFP4) {
+          const v4i x4 = *reinterpret_cast<const v4i*>(rowp + 16 * ((C::S * g + s) ^ swz<C::CA>(r)));
+          af[f] = v8i{x4[0], x4[1], x4[2], x4[3], 0, 0, 0, 0};
+        } else {
+          const v4i lo = *reinterpret_cast<const v4i*>(rowp + 16 * ((2 * s + g) ^ swz<C::CA>(r)));
+          const v4i hi = *reinterpret_cast<const v4i*>(rowp + 16 * ((2 * (C::S + s) + g) ^ swz<C::CA>(r)));
+          af[f] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        const int rb = brow_l[f];
+        const v4i y4 = *reinterpret_cast<const v4i*>(&sl.B[rb * C::RB + 16 * ((C::S * g + s) ^ swz<C::CB>(rb))]);
+        bf[f] = v8i{y4[0], y4[1], y4[2], y4[3], 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) {
+          if (s == 0) acc[fm][fn] = mfma32x32x64<kFA, kFmtFP4, 0>(af[fm], bf[fn], acc[fm][fn], sa[fm], sb[fn]);
+          else if (s == 1) acc[fm][fn] = mfma32x32x64<kFA, kFmtFP4, 1>(af[fm], bf[fn], acc[fm][fn], sa[fm], sb[fn]);
+          else if (s == 2) acc[fm][fn] = mfma32x32x64<kFA, kFmtFP4, 2>(af[fm], bf[fn], acc[fm][fn], sa[fm], sb[fn]);
+          else acc[fm][fn] = mfma32x32x64<kFA, kFmtFP4, 3>(af[fm], bf[fn], acc[fm][fn], sa[fm], sb[fn]);
+        }
+    }
+  };
+
+  // ring: at stage st, stages st .. st+NS-2 have been issued; wait for st (leaving
+  // the later ones in flight), barrier, refill the slot freed by st-1, compute st
+  constexpr int NS = C::NS;
+  const int nst = NST > 0 ? NST : (int)(K / C::KS);
+  auto slot_of = [&](auto I) -> T3Slot<kActFP4>& {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) {
+      return slot0;
+    } else if constexpr (i == 1) {
+      return slot1;
+    } else {
+      if constexpr (kActFP4) return slot2;
+      else return slot0;  // never reached: FP8 runs a 2-slot ring
+    }
+  };
+  auto step = [&](auto I, int st) {
+    constexpr int i = decltype(I)::value;
+    constexpr int inext = (i + NS - 1) % NS;
+    if (NS == 3 && st + 1 < nst) wait_vmcnt<C8::D>();  // stage st+1 (issued after st) may stay in flight
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (st + NS - 1 < nst) issue(slot_of(std::integral_constant<int, inext>{}), st + NS - 1);
+    compute(slot_of(I));
+  };
+  issue(slot0, 0);
+  if constexpr (NS == 3) {
+    if (nst > 1) issue(slot1, 1);
+  }
+  auto ring_turn = [&](int st0) {
+    step(std::integral_constant<int, 0>{}, st0);
+    if (st0 + 1 < nst) step(std::integral_constant<int, 1>{}, st0 + 1);
+    if constexpr (NS == 3) {
+      if (st0 + 2 < nst) step(std::integral_constant<int, 2>{}, st0 + 2);
+    }
+  };
+  if constexpr (NST > 0) {
+#pragma unroll
+    for (int st0 = 0; st0 < NST; st0 += NS) ring_turn(st0);
+  } else {
+    for (int st0 = 0; st0 < nst; st0 += NS) ring_turn(st0);
+  }
+  lds_barrier();  // every wave is done reading the ring; the slots become staging areas
+
+  // wave w stages in slot0 (w < 4) or slot1 (w >= 4), region (w % 4) x 9216 bytes
+  uint8_t* const stage = (wave < 4 ? slot0.A : slot1.A) + (wave & 3) * 9216;
+  static_assert(4 * 9216 <= (int)sizeof(T3Slot<kActFP4>), "per-wave staging regions must fit a slot");
+  auto lds_wave_fence = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+  if (kMode == kModeFC1) {
+    // h = silu(gate) * up: 64 rows x 32 I-columns (one quantisation block per row),
+    // then lane l requantises row l
+    float(*hf)[36] = reinterpret_cast<float(*)[36]>(stage);
+    const int64_t icol = (int64_t)n_tile * (BN / 2) + 32 * wn;
+    const int64_t hrow = kActFP4 ? a.I / 2 : a.I;
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        hf[32 * fm + 8 * (v >> 2) + 4 * g + (v & 3)][r32] = silu_mul(acc[fm][0][v], acc[fm][1][v]);
+    lds_wave_fence();
+    const int lr = 64 * wm + lane;
+    if (lr < m) {
+      const int64_t R = row0 + lr;
+      quantize_store32<kActFP4>(&hf[lane][0], a.h + R * hrow + icol / (kActFP4 ? 2 : 1),
+                                a.h_scale + R * (a.I / 32) + icol / 32);
+    }
+  } else if (kYBF16) {
+    uint16_t(*ob)[72] = reinterpret_cast<uint16_t(*)[72]>(stage);  // 64 x 72 x 2 = 9216 bytes
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    const int64_t col0 = (int64_t)n_tile * BN + 64 * wn;
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          ob[32 * fm + 8 * (v >> 2) + 4 * g + (v & 3)][32 * fn + r32] = (uint16_t)bf16_round(acc[fm][fn][v]);
+    lds_wave_fence();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // 64 rows x 64 columns = 512 pieces of 16 bytes
+      const int idx = lane + 64 * j;
+      const int rr = idx >> 3, c8 = idx & 7;
+      const int lr = 64 * wm + rr;
+      if (lr < m)
+        *reinterpret_cast<uint4*>(out + (row0 + lr) * a.N + col0 + 8 * c8) = *reinterpret_cast<const uint4*>(&ob[rr][8 * c8]);
+    }
+  } else {
+    float(*of)[68] = reinterpret_cast<float(*)[68]>(stage);  // 32 x 68 x 4 = 8704 bytes
+    float* out = static_cast<float*>(a.out);
+    const int64_t col0 = (int64_t)n_tile * BN + 64 * wn;
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) {
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) of[8 * (v >> 2) + 4 * g + (v & 3)][32 * fn + r32] = acc[fm][fn][v];
+      lds_wave_fence();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {  // 32 rows x 64 columns = 512 pieces of 16 bytes
+        const int idx = lane + 64 * j;
+        const int rr = idx >> 4, c4 = idx & 15;
+        const int lr = 64 * wm + 32 * fm + rr;
+        if (lr < m)
+          *reinterpret_cast<float4*>(out + (row0 + lr) * a.N + col0 + 4 * c4) = *reinterpret_cast<const float4*>(&of[rr][4 * c4]);
+      }
+      lds_wave_fence();
+    }
+  }
+}
+
+template <bool kActFP4, int kMode, bool kYBF16>
+static void launch_tile8(const GemmArgs& a, int64_t m_units, hipStream_t stream) {
+  const int64_t nn = cdiv(a.ntiles, 8);
+  const dim3 grid((unsigned)(8 * nn * m_units));
+  const int64_t nst = a.K / 256;
+  if (nst == 28) gemm_tile8_kernel<kActFP4, kMode, kYBF16, 28><<<grid, 512, 0, stream>>>(a);
+  else if (nst == 8) gemm_tile8_kernel<kActFP4, kMode, kYBF16, 8><<<grid, 512, 0, stream>>>(a);
+  else gemm_tile8_kernel<kActFP4, kMode, kYBF16, 0><<<grid, 512, 0, stream>>>(a);
+}
+
+#ifndef MXF_TILE8
+#define MXF_TILE8 1
+#endif
+
 template <bool kActFP4, int kMode, bool kYBF16>
 static void launch_tile3(const GemmArgs& a, int64_t m_units, hipStream_t stream) {
   const int64_t nn3 = cdiv(a.ntiles, 8);
@@ -668,6 +938,13 @@ static void launch_tile_fmt(int mode, bool y_bf16, const GemmArgs& a, int64_t m_
     else if (mode == kModeDense) launch_tile4<kActFP4, kModeDense, false>(a, m_units, stream);
     else if (y_bf16) launch_tile4<kActFP4, kModeFC2, true>(a, m_units, stream);
     else launch_tile4<kActFP4, kModeFC2, false>(a, m_units, stream);
+    return;
+  }
+  if (MXF_TILE8) {
+    if (mode == kModeFC1) launch_tile8<kActFP4, kModeFC1, false>(a, m_units, stream);
+    else if (mode == kModeDense) launch_tile8<kActFP4, kModeDense, false>(a, m_units, stream);
+    else if (y_bf16) launch_tile8<kActFP4, kModeFC2, true>(a, m_units, stream);
+    else launch_tile8<kActFP4, kModeFC2, false>(a, m_units, stream);
     return;
   }
   if (mode == kModeFC1) launch_tile3<kActFP4, kModeFC1, false>(a, m_units, stream);
