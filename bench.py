@@ -47,7 +47,7 @@ TRAFFIC_SRC_SHA256 = "123f63900cb781546edffd7c1c0063debe44c5e96bd57712476ed576ac
 TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 12361979904, "moe_decode_t8": 1030335488}
 
 
-GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip")
+GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip")
 
 
 def gemm_sources_sha256():

@@ -126,20 +126,24 @@ __global__ void __launch_bounds__(256) gemm_tile3_kernel(GemmArgs a) {
     psb[q] = a.w_scale + ((int64_t)e * a.N + b_row(r)) * srow + 4 * part;
   }
 
+  // copy j (0 .. D-1) of stage st into slot sl: A chunks, B chunks, A scales, B scales
+  auto issue_one = [&](T3Slot<kActFP4>& sl, int st, int j) {
+    if (j < C::IA) {
+      dma16_to_lds(pa[j] + (int64_t)st * C::RA, &sl.A[(wave * C::IA + j) * 1024]);
+    } else if (j < C::IA + C::IB) {
+      const int q = j - C::IA;
+      dma16_to_lds(pb[q] + (int64_t)st * C::RB, &sl.B[(wave * C::IB + q) * 1024]);
+    } else if (j < C::IA + C::IB + C::ISA) {
+      const int q = j - C::IA - C::IB;
+      dma4_to_lds(psa[q] + (int64_t)st * C::SB, &sl.As[(wave * C::ISA + q) * 256]);
+    } else {
+      const int q = j - C::IA - C::IB - C::ISA;
+      dma4_to_lds(psb[q] + (int64_t)st * C::SB, &sl.Bs[(wave * C::ISB + q) * 256]);
+    }
+  };
   auto issue = [&](T3Slot<kActFP4>& sl, int st) {
-    const int64_t oa = (int64_t)st * C::RA, ob = (int64_t)st * C::RB, os = (int64_t)st * C::SB;
 #pragma unroll
-    for (int q = 0; q < C::IA; ++q)
-      dma16_to_lds(pa[q] + oa, &sl.A[(wave * C::IA + q) * 1024]);
-#pragma unroll
-    for (int q = 0; q < C::IB; ++q)
-      dma16_to_lds(pb[q] + ob, &sl.B[(wave * C::IB + q) * 1024]);
-#pragma unroll
-    for (int q = 0; q < C::ISA; ++q)
-      dma4_to_lds(psa[q] + os, &sl.As[(wave * C::ISA + q) * 256]);
-#pragma unroll
-    for (int q = 0; q < C::ISB; ++q)
-      dma4_to_lds(psb[q] + os, &sl.Bs[(wave * C::ISB + q) * 256]);
+    for (int j = 0; j < C::D; ++j) issue_one(sl, st, j);
   };
 
   v16f acc[2][4];
@@ -157,7 +161,11 @@ __global__ void __launch_bounds__(256) gemm_tile3_kernel(GemmArgs a) {
     else brow_l[f] = 128 * wn + 32 * f + r32;
   }
 
-  auto compute = [&](const T3Slot<kActFP4>& sl) {
+  // compute one stage; ahead of MFMA step s go copies [s DC, (s + 1) DC) of the
+  // next stage (when nsl is given), so the copies spread over the stage instead
+  // of stalling the wave in one burst
+  constexpr int DC = (C::D + C::S - 1) / C::S;
+  auto compute = [&](const T3Slot<kActFP4>& sl, T3Slot<kActFP4>* nsl, int nst_) {
     int sa[2], sb[4];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
@@ -171,6 +179,11 @@ __global__ void __launch_bounds__(256) gemm_tile3_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int s = 0; s < C::S; ++s) {
+      if (nsl) {
+#pragma unroll
+        for (int j = s * DC; j < (s + 1) * DC && j < C::D; ++j) issue_one(*nsl, nst_, j);
+      }
+      __builtin_amdgcn_sched_barrier(0x078F);  // the copies stay in this step; all else may move
       v8i af[2], bf[4];
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
@@ -229,8 +242,7 @@ __global__ void __launch_bounds__(256) gemm_tile3_kernel(GemmArgs a) {
     if (NS == 3 && st + 1 < nst) wait_vmcnt<D>();  // stage st+1 may stay in flight
     else wait_vmcnt<0>();
     lds_barrier();
-    if (st + NS - 1 < nst) issue(slot_of(std::integral_constant<int, inext>{}), st + NS - 1);
-    compute(slot_of(I));
+    compute(slot_of(I), st + NS - 1 < nst ? &slot_of(std::integral_constant<int, inext>{}) : nullptr, st + NS - 1);
   };
   issue(slot0, 0);
   if constexpr (NS == 3) {
@@ -724,14 +736,22 @@ __global__ void __launch_bounds__(512) gemm_tile8_kernel(GemmArgs a) {
   const uint8_t* psa = a.act_scale + a_src_row(16 * wave + ((lane & 31) >> 1)) * srow + 4 * (lane & 1);
   const uint8_t* psb = a.w_scale + ((int64_t)e * a.N + b_row(32 * wave + (lane >> 1))) * srow + 4 * (lane & 1);
 
+  // copy j (0 .. D-1) of stage st into slot sl: A chunks, B chunks, A scales, B scales
+  auto issue_one = [&](T3Slot<kActFP4>& sl, int st, int j) {
+    if (j < C8::IA) {
+      dma16_to_lds(pa[j] + (int64_t)st * C::RA, &sl.A[(wave * C8::IA + j) * 1024]);
+    } else if (j < C8::IA + C8::IB) {
+      const int q = j - C8::IA;
+      dma16_to_lds(pb[q] + (int64_t)st * C::RB, &sl.B[(wave * C8::IB + q) * 1024]);
+    } else if (j == C8::IA + C8::IB) {
+      if (lane < 32) dma4_to_lds(psa + (int64_t)st * C::SB, &sl.As[wave * 128]);  // one instruction, half the lanes
+    } else {
+      dma4_to_lds(psb + (int64_t)st * C::SB, &sl.Bs[wave * 256]);
+    }
+  };
   auto issue = [&](T3Slot<kActFP4>& sl, int st) {
-    const int64_t oa = (int64_t)st * C::RA, ob = (int64_t)st * C::RB, os = (int64_t)st * C::SB;
 #pragma unroll
-    for (int q = 0; q < C8::IA; ++q) dma16_to_lds(pa[q] + oa, &sl.A[(wave * C8::IA + q) * 1024]);
-#pragma unroll
-    for (int q = 0; q < C8::IB; ++q) dma16_to_lds(pb[q] + ob, &sl.B[(wave * C8::IB + q) * 1024]);
-    if (lane < 32) dma4_to_lds(psa + os, &sl.As[wave * 128]);  // one instruction, half the lanes
-    dma4_to_lds(psb + os, &sl.Bs[wave * 256]);
+    for (int j = 0; j < C8::D; ++j) issue_one(sl, st, j);
   };
 
   v16f acc[2][2];
@@ -747,7 +767,10 @@ __global__ void __launch_bounds__(512) gemm_tile8_kernel(GemmArgs a) {
     else brow_l[f] = 64 * wn + 32 * f + r32;
   }
 
-  auto compute = [&](const T3Slot<kActFP4>& sl) {
+  // compute one stage; ahead of MFMA step s go copies [s DC, (s + 1) DC) of the
+  // next stage (when nsl is given), so the copies spread over the stage
+  constexpr int DC = (C8::D + C::S - 1) / C::S;
+  auto compute = [&](const T3Slot<kActFP4>& sl, T3Slot<kActFP4>* nsl, int nst_) {
     int sa[2], sb[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
@@ -756,6 +779,11 @@ __global__ void __launch_bounds__(512) gemm_tile8_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int s = 0; s < C::S; ++s) {
+      if (nsl) {
+#pragma unroll
+        for (int j = s * DC; j < (s + 1) * DC && j < C8::D; ++j) issue_one(*nsl, nst_, j);
+      }
+      __builtin_amdgcn_sched_barrier(0x078F);  // the copies stay in this step; all else may move
       v8i af[2], bf[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
@@ -806,8 +834,7 @@ __global__ void __launch_bounds__(512) gemm_tile8_kernel(GemmArgs a) {
     if (NS == 3 && st + 1 < nst) wait_vmcnt<C8::D>();  // stage st+1 (issued after st) may stay in flight
     else wait_vmcnt<0>();
     lds_barrier();
-    if (st + NS - 1 < nst) issue(slot_of(std::integral_constant<int, inext>{}), st + NS - 1);
-    compute(slot_of(I));
+    compute(slot_of(I), st + NS - 1 < nst ? &slot_of(std::integral_constant<int, inext>{}) : nullptr, st + NS - 1);
   };
   issue(slot0, 0);
   if constexpr (NS == 3) {
@@ -953,8 +980,20 @@ static void launch_tile_fmt(int mode, bool y_bf16, const GemmArgs& a, int64_t m_
   else launch_tile3<kActFP4, kModeFC2, false>(a, m_units, stream);
 }
 
-void launch_tile_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int64_t m_units,
+#ifndef MXF_WIDE
+#define MXF_WIDE 1
+#endif
+
+void launch_tile_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int64_t rows, int64_t groups,
                       hipStream_t stream) {
+  // the wide kernel addresses activations and one expert's weights with 32-bit byte offsets
+  const int64_t lim = (int64_t)1 << 32;
+  if (MXF_WIDE && act_fp4 && a.act_rows * (a.K / 2) < lim && a.N * (a.K / 2) < lim) {
+    // 256-row units: an upper bound on the units summed over the groups
+    launch_wide_gemm(mode, y_bf16, a, cdiv(rows, 256) + groups, stream);
+    return;
+  }
+  const int64_t m_units = cdiv(rows, tile::BM) + groups;
   if (act_fp4) launch_tile_fmt<true>(mode, y_bf16, a, m_units, stream);
   else launch_tile_fmt<false>(mode, y_bf16, a, m_units, stream);
 }

@@ -1,0 +1,332 @@
+// Wide LDS-ring MXFP4 GEMM for E2M1 activations: 256 activation rows x 256 weight
+// rows per workgroup, 8 waves of 64 x 128 on the 32x32x64 scaled MFMA.
+//
+// Why a second ring kernel: with FP4 x FP4 operands a 128 x 256 tile moves 51 KB
+// from L2 into LDS per 256-k stage for 128 MFMAs, which at the matrix cores' rate
+// asks for about 46 bytes per clock per CU - the measured ceiling of the
+// L2 -> LDS copy path. A 256 x 256 tile moves 68 KB for 256 MFMAs (two thirds of
+// the bytes per product), so the copy path stops being the limit. Two 68 KB slots
+// fill most of the 160 KB of LDS, so the ring is two stages deep: the copies of
+// stage st+1 are issued while stage st is computed, spread over its four MFMA steps.
+//
+// Row groups of 64 that lie wholly past an expert's last row skip their MFMAs (the
+// wave still issues its share of the copies and meets every barrier), so the
+// padding of a 256-row unit costs copy bandwidth but not matrix-core time.
+#include "gemm_common.hpp"
+
+namespace mxf {
+
+namespace wide {
+constexpr int BM = 256, BN = 256;
+constexpr int KS = 256;                  // k per stage
+constexpr int S = KS / 64;               // MFMA steps per stage
+constexpr int R = KS / 2;                // bytes per row per stage (E2M1, A and B alike)
+constexpr int CH = R / 16;               // 16-byte chunks per row
+constexpr int SB = KS / 32;              // scale bytes per row per stage
+constexpr int IA = BM * CH / 64 / 8;     // A copies (16 B per lane) per wave per stage
+constexpr int IB = BN * CH / 64 / 8;     // B copies per wave per stage
+constexpr int D = IA + IB + 2;           // + one A-scale and one B-scale copy (4 B per lane)
+constexpr int STG = 8704;                // epilogue staging bytes per wave
+}  // namespace wide
+
+struct alignas(16) WideSlot {
+  uint8_t A[wide::BM * wide::R];
+  uint8_t B[wide::BN * wide::R];
+  uint8_t As[wide::BM * wide::SB];
+  uint8_t Bs[wide::BN * wide::SB];
+};
+static_assert(2 * sizeof(WideSlot) <= 160 * 1024, "two ring slots must fit in LDS");
+static_assert(4 * wide::STG <= (int)sizeof(WideSlot), "four waves' staging regions must fit a slot");
+
+// NST > 0: K / 256 is a compile-time constant and the ring is fully unrolled;
+// NST == 0: any K (multiple of 256) with a runtime loop.
+template <int kMode, bool kYBF16, int NST>
+__global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
+  using namespace wide;
+  __shared__ WideSlot slot0, slot1;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;  // rows [64 wm, 64 wm + 64), column half wn
+
+  // XCD-aware order (block b runs on XCD b % 8): XCD x owns n-tiles [x*nt/8, (x+1)*nt/8)
+  const int ntiles = a.ntiles;
+  const int x = (int)(blockIdx.x & 7u), jb = (int)(blockIdx.x >> 3);
+  const int n_lo = x * ntiles / 8, n_hi = (x + 1) * ntiles / 8, nn = n_hi - n_lo;
+  if (nn == 0) return;
+  const int m_unit = jb / nn;
+  const int n_tile = n_lo + jb % nn;
+
+  int e = 0;
+  int64_t row0;
+  int m;
+  if (kMode == kModeDense) {
+    row0 = (int64_t)m_unit * BM;
+    if (row0 >= a.M) return;
+    m = (int)(a.M - row0 < BM ? a.M - row0 : BM);
+  } else {
+    int loc;
+    find_unit<BM>(a.offsets, a.E, m_unit, e, loc);
+    if (e < 0) return;
+    row0 = a.offsets[e] + (int64_t)loc * BM;
+    m = min(BM, a.offsets[e + 1] - (int)row0);
+  }
+  const int64_t K = a.K;
+  const int64_t wrow = K / 2, srow = K / 32;
+
+  auto a_src_row = [&](int r) -> int64_t {  // rows past m read the unit's first row (never stored)
+    if (r >= m) r = 0;
+    return (kMode == kModeFC1) ? (int64_t)(a.sorted_pair[row0 + r] / a.topk) : row0 + r;
+  };
+  // FC1: weight rows [0, 128) of the tile are gate rows, [128, 256) the matching up rows
+  auto b_row = [&](int r) -> int64_t {
+    if (kMode == kModeFC1) return (r < BN / 2 ? 0 : a.I - BN / 2) + (int64_t)n_tile * (BN / 2) + r;
+    return (int64_t)n_tile * BN + r;
+  };
+
+  // per-lane copy sources as 32-bit byte offsets into range-checked buffer
+  // resources (activations, this expert's weights, their scales); LDS chunk c of a
+  // slot holds row c / 8, global chunk (c % 8) ^ swz(row) of that row's 128-byte
+  // stage segment. The expert index is wave-uniform; readfirstlane makes the
+  // compiler see that, so the resources live in scalar registers.
+  const int eu = __builtin_amdgcn_readfirstlane(e);
+  const buf_rsrc ra = make_rsrc(a.act, (uint32_t)(a.act_rows * wrow));
+  const buf_rsrc ras = make_rsrc(a.act_scale, (uint32_t)(a.act_rows * srow));
+  const buf_rsrc rb = make_rsrc(a.w + (int64_t)eu * a.N * wrow, (uint32_t)(a.N * wrow));
+  const buf_rsrc rbs = make_rsrc(a.w_scale + (int64_t)eu * a.N * srow, (uint32_t)(a.N * srow));
+  uint32_t va[IA], vb[IB];
+#pragma unroll
+  for (int q = 0; q < IA; ++q) {
+    const int chunk = (wave * IA + q) * 64 + lane;
+    const int r = chunk / CH, pc = chunk % CH;
+    va[q] = (uint32_t)(a_src_row(r) * wrow + 16 * (pc ^ swz<CH>(r)));
+  }
+#pragma unroll
+  for (int q = 0; q < IB; ++q) {
+    const int chunk = (wave * IB + q) * 64 + lane;
+    const int r = chunk / CH, pc = chunk % CH;
+    vb[q] = (uint32_t)(b_row(r) * wrow + 16 * (pc ^ swz<CH>(r)));
+  }
+  // scale copies in 4-byte pieces, lane l's piece landing at 4 l: wave w fills rows
+  // [32 w, 32 w + 32) of the [256][8] A-scale and B-scale slots
+  const uint32_t vsa = (uint32_t)(a_src_row(32 * wave + (lane >> 1)) * srow + 4 * (lane & 1));
+  const uint32_t vsb = (uint32_t)(b_row(32 * wave + (lane >> 1)) * srow + 4 * (lane & 1));
+
+  // copy j (0 .. D-1) of stage st into slot sl: A chunks, B chunks, A scales, B scales
+  auto issue_one = [&](WideSlot& sl, int st, int j) {
+    if (j < IA) {
+      buf_dma16(ra, &sl.A[(wave * IA + j) * 1024], va[j], (uint32_t)st * R);
+    } else if (j < IA + IB) {
+      const int q = j - IA;
+      buf_dma16(rb, &sl.B[(wave * IB + q) * 1024], vb[q], (uint32_t)st * R);
+    } else if (j == IA + IB) {
+      buf_dma4(ras, &sl.As[wave * 256], vsa, (uint32_t)st * SB);
+    } else {
+      buf_dma4(rbs, &sl.Bs[wave * 256], vsb, (uint32_t)st * SB);
+    }
+  };
+
+  v16f acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+  int arow_l[2], brow_l[4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) arow_l[f] = 64 * wm + 32 * f + r32;
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    // FC1: fragments 0, 1 are gate columns [64 wn, 64 wn + 64), 2, 3 the matching up columns
+    if (kMode == kModeFC1) brow_l[f] = (f < 2 ? 0 : BN / 2) + 64 * wn + 32 * (f & 1) + r32;
+    else brow_l[f] = 128 * wn + 32 * f + r32;
+  }
+
+  // MFMA step s of a stage covers, for lane group g, the 32-k block 4 g + s (16-byte
+  // chunk 4 g + s of a row; byte s of the lane's scale dword)
+  struct Frags {
+    v4i a[2], b[4];
+  };
+  auto load_frags = [&](const WideSlot& sl, int s, Frags& F) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int r = arow_l[f];
+      F.a[f] = *reinterpret_cast<const v4i*>(&sl.A[r * R + 16 * ((4 * g + s) ^ swz<CH>(r))]);
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int r = brow_l[f];
+      F.b[f] = *reinterpret_cast<const v4i*>(&sl.B[r * R + 16 * ((4 * g + s) ^ swz<CH>(r))]);
+    }
+  };
+  auto mfma_step = [&](auto S_, const Frags& F, const int* sa, const int* sb) {
+    constexpr int s = decltype(S_)::value;
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) {
+      const v8i af = v8i{F.a[fm][0], F.a[fm][1], F.a[fm][2], F.a[fm][3], 0, 0, 0, 0};
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn) {
+        const v8i bf = v8i{F.b[fn][0], F.b[fn][1], F.b[fn][2], F.b[fn][3], 0, 0, 0, 0};
+        acc[fm][fn] = mfma32x32x64<kFmtFP4, kFmtFP4, s>(af, bf, acc[fm][fn], sa[fm], sb[fn]);
+      }
+    }
+  };
+
+  // One stage. Step s issues copies [s DC, (s + 1) DC) of stage nst_ into slot nsl
+  // (when `more`), reads the fragments of step s + 1 and runs the MFMAs of step s;
+  // full scheduling fences between the steps keep that order, so the copies spread
+  // over the stage and each step's LDS reads overlap the previous step's MFMAs.
+  constexpr int DC = (D + S - 1) / S;
+  auto stage = [&](auto kActive, const WideSlot& sl, WideSlot& nsl, bool more, int nst_) {
+    constexpr bool act = decltype(kActive)::value;
+    int sa[2], sb[4];
+    Frags F[2];
+    if constexpr (act) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) sa[f] = *reinterpret_cast<const int*>(&sl.As[arow_l[f] * SB + 4 * g]);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) sb[f] = *reinterpret_cast<const int*>(&sl.Bs[brow_l[f] * SB + 4 * g]);
+      load_frags(sl, 0, F[0]);
+    }
+    auto one = [&](auto S_) {
+      constexpr int s = decltype(S_)::value;
+      if (more) {
+#pragma unroll
+        for (int j = s * DC; j < (s + 1) * DC && j < D; ++j) issue_one(nsl, nst_, j);
+      }
+      if constexpr (act) {
+        if constexpr (s + 1 < S) load_frags(sl, s + 1, F[(s + 1) & 1]);
+        mfma_step(S_, F[s & 1], sa, sb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    one(std::integral_constant<int, 0>{});
+    one(std::integral_constant<int, 1>{});
+    one(std::integral_constant<int, 2>{});
+    one(std::integral_constant<int, 3>{});
+  };
+  static_assert(S == 4, "four MFMA steps per stage");
+
+  // ring of two slots: at stage st wait for its copies (the only ones in flight),
+  // barrier (every wave's part has landed and every wave is done with st - 1),
+  // then compute st while the copies of st + 1 go to the other slot
+  const int nst = NST > 0 ? NST : (int)(K / KS);
+  auto run = [&](auto kActive) {
+    auto step = [&](auto I, int st) {
+      constexpr int i = decltype(I)::value;
+      wait_vmcnt<0>();
+      lds_barrier();
+      WideSlot& cur = i == 0 ? slot0 : slot1;
+      WideSlot& nxt = i == 0 ? slot1 : slot0;
+      stage(kActive, cur, nxt, st + 1 < nst, st + 1);
+    };
+    auto turn = [&](int st0) {
+      step(std::integral_constant<int, 0>{}, st0);
+      if (st0 + 1 < nst) step(std::integral_constant<int, 1>{}, st0 + 1);
+    };
+    if constexpr (NST > 0) {
+#pragma unroll
+      for (int st0 = 0; st0 < NST; st0 += 2) turn(st0);
+    } else {
+      for (int st0 = 0; st0 < nst; st0 += 2) turn(st0);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < D; ++j) issue_one(slot0, 0, j);
+  if (64 * wm < __builtin_amdgcn_readfirstlane(m)) run(std::true_type{});
+  else run(std::false_type{});
+  lds_barrier();  // every wave is done reading the ring; the slots become staging areas
+
+  // wave w stages in slot0 (w < 4) or slot1 (w >= 4), region (w % 4) x STG bytes;
+  // the staging writes and reads are this wave's own
+  uint8_t* const stg = (wave < 4 ? slot0.A : slot1.A) + (wave & 3) * STG;
+  auto lds_wave_fence = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+  if (64 * wm >= m) return;
+  if (kMode == kModeFC1) {
+    // h = silu(gate) * up for 32 rows x 64 I-columns at a time (two quantisation
+    // blocks per row); lane l requantises block l % 2 of row l / 2
+    float(*hf)[68] = reinterpret_cast<float(*)[68]>(stg);
+    const int64_t icol = (int64_t)n_tile * (BN / 2) + 64 * wn;
+    const int64_t hrow = a.I / 2;
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          hf[8 * (v >> 2) + 4 * g + (v & 3)][32 * f + r32] = silu_mul(acc[fm][f][v], acc[fm][f + 2][v]);
+      lds_wave_fence();
+      const int lr = 64 * wm + 32 * fm + (lane >> 1), blk = lane & 1;
+      if (lr < m) {
+        const int64_t Rw = row0 + lr;
+        quantize_store32<true>(&hf[lane >> 1][32 * blk], a.h + Rw * hrow + (icol + 32 * blk) / 2,
+                               a.h_scale + Rw * (a.I / 32) + (icol + 32 * blk) / 32);
+      }
+      lds_wave_fence();
+    }
+  } else if (kYBF16) {
+    uint16_t(*ob)[136] = reinterpret_cast<uint16_t(*)[136]>(stg);  // 32 x 136 x 2 = 8704 bytes
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    const int64_t col0 = (int64_t)n_tile * BN + 128 * wn;
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) {
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          ob[8 * (v >> 2) + 4 * g + (v & 3)][32 * fn + r32] = (uint16_t)bf16_round(acc[fm][fn][v]);
+      lds_wave_fence();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {  // 32 rows x 128 columns = 512 pieces of 16 bytes
+        const int idx = lane + 64 * j;
+        const int rr = idx >> 4, c8 = idx & 15;
+        const int lr = 64 * wm + 32 * fm + rr;
+        if (lr < m)
+          *reinterpret_cast<uint4*>(out + (row0 + lr) * a.N + col0 + 8 * c8) =
+              *reinterpret_cast<const uint4*>(&ob[rr][8 * c8]);
+      }
+      lds_wave_fence();
+    }
+  } else {
+    float(*of)[68] = reinterpret_cast<float(*)[68]>(stg);  // 32 x 68 x 4 = 8704 bytes
+    float* out = static_cast<float*>(a.out);
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {  // column fragments 2 p, 2 p + 1
+        const int64_t col0 = (int64_t)n_tile * BN + 128 * wn + 64 * p;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) of[8 * (v >> 2) + 4 * g + (v & 3)][32 * h + r32] = acc[fm][2 * p + h][v];
+        lds_wave_fence();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {  // 32 rows x 64 columns = 512 pieces of 16 bytes
+          const int idx = lane + 64 * j;
+          const int rr = idx >> 4, c4 = idx & 15;
+          const int lr = 64 * wm + 32 * fm + rr;
+          if (lr < m)
+            *reinterpret_cast<float4*>(out + (row0 + lr) * a.N + col0 + 4 * c4) =
+                *reinterpret_cast<const float4*>(&of[rr][4 * c4]);
+        }
+        lds_wave_fence();
+      }
+  }
+}
+
+template <int kMode, bool kYBF16>
+static void launch_wide_t(const GemmArgs& a, int64_t m_units, hipStream_t stream) {
+  const dim3 grid((unsigned)(8 * cdiv(a.ntiles, 8) * m_units));
+  // fully unrolled instances for K = 7168 and K = 2048 (the layer's H and I)
+  const int64_t nst = a.K / wide::KS;
+  if (nst == 28) gemm_wide_kernel<kMode, kYBF16, 28><<<grid, 512, 0, stream>>>(a);
+  else if (nst == 8) gemm_wide_kernel<kMode, kYBF16, 8><<<grid, 512, 0, stream>>>(a);
+  else gemm_wide_kernel<kMode, kYBF16, 0><<<grid, 512, 0, stream>>>(a);
+}
+
+void launch_wide_gemm(int mode, bool y_bf16, const GemmArgs& a, int64_t m_units, hipStream_t stream) {
+  if (mode == kModeFC1) launch_wide_t<kModeFC1, false>(a, m_units, stream);
+  else if (mode == kModeDense) launch_wide_t<kModeDense, false>(a, m_units, stream);
+  else if (y_bf16) launch_wide_t<kModeFC2, true>(a, m_units, stream);
+  else launch_wide_t<kModeFC2, false>(a, m_units, stream);
+}
+
+}  // namespace mxf

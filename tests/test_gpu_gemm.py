@@ -31,6 +31,9 @@ def test_dense_workloads(name):
     (1, 16, 512, "e4m3"), (5, 48, 1024, "e4m3"), (17, 64, 2048, "e2m1"), (63, 80, 512, "e4m3"),
     (70, 256, 1536, "e4m3"),  # M > 64 with N % 256 == 0 -> LDS-tiled kernel, ragged last tile
     (300, 384, 1024, "e2m1"), (129, 96, 512, "e4m3"),  # M > 64, N % 256 != 0 -> streamed in 64-row chunks
+    # E2M1 activations, M > 64, N % 256 == 0 -> 256 x 256 tiles: a 44-row tail unit (runtime
+    # stage loop, K = 1536) and an 8-row tail unit whose other row groups skip their MFMAs (K = 2048)
+    (300, 512, 1536, "e2m1"), (520, 256, 2048, "e2m1"),
     # M <= 64 with more than 4 super-steps of 512 k: K split into slices summed in a fixed order
     (33, 48, 5120, "e2m1"),   # 3 slices, the last with 2 super-steps (two idle waves)
     (64, 96, 2560, "e4m3"),   # 2 slices, the last with 1 super-step

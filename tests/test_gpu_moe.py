@@ -63,6 +63,7 @@ def _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt, rows=None, tokens=None):
     (300, 1024, 512, 8, 6, "e4m3", 2),     # LDS-tiled kernel, several 128-row tiles, ragged tails
     (333, 1024, 1024, 32, 4, "e2m1", 3),   # FP4 x FP4 tiles, some experts empty
     (65, 512, 512, 4, 2, "e4m3", 4),       # just past the streaming threshold
+    (700, 2048, 512, 4, 2, "e2m1", 5),     # FP4 x FP4, ~350 rows per expert: full and partial 256-row units
 ])
 def test_layer_small_shapes_full_oracle(T, H, I, E, k, fmt, seed):
     x = dg.activations(seed, T, H)
@@ -92,6 +93,16 @@ def test_layer_fp32_y():
     g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, "e4m3", y_dtype=torch.float32)
     ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e4m3")
     _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e4m3")
+
+
+def test_layer_fp32_y_fp4_tiles():
+    T, H, I, E, k = 300, 1024, 512, 8, 4
+    x = dg.activations(13, T, H)
+    logits = dg.logits(13, T, E, "normal")
+    w1, s1, w2, s2 = dg.moe_weights(13, E, H, I, 120, 128)
+    g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, "e2m1", y_dtype=torch.float32)
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e2m1")
+    _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e2m1")
 
 
 @pytest.mark.parametrize("name,ntok", [("moe_decode_t8", None), ("moe_prefill_t2048_zipf", 6),
