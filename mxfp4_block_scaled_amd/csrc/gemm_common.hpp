@@ -95,7 +95,14 @@ __device__ __forceinline__ void find_unit(const int32_t* __restrict__ off, int E
   loc_out = __shfl(loc, src);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u with the hardware exponential and reciprocal (about 1 ulp each)
+__device__ __forceinline__ float silu_mul(float g, float u) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+#else
+  return g / (1.0f + __expf(-g)) * u;
+#endif
+}
 
 template <bool kYBF16>
 __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {

@@ -38,6 +38,71 @@ struct alignas(16) WideSlot {
 static_assert(2 * sizeof(WideSlot) <= 160 * 1024, "two ring slots must fit in LDS");
 static_assert(4 * wide::STG <= (int)sizeof(WideSlot), "four waves' staging regions must fit a slot");
 
+#ifndef MXF_WIDE_ORDER
+#define MXF_WIDE_ORDER 1
+#endif
+
+// Work item of block j on XCD x for the grouped GEMMs. Items run expert by expert;
+// within an expert, n-tile by n-tile, and within an n-tile over the expert's units,
+// so the workgroups resident on one XCD at a time cover one or two experts: each
+// activation unit is shared by every n-tile there and each weight tile by the
+// expert's units, and L2 holds both. The U * ntiles items are split into 8
+// contiguous ranges, one per XCD (block b runs on XCD b % 8). Called by a whole
+// wave; the results are wave-uniform. e_out < 0: no item for this block.
+__device__ __forceinline__ void wide_work_item(const int32_t* __restrict__ off, int E, int ntiles, int x, int j,
+                                               int& e_out, int& n_out, int& loc_out) {
+  constexpr int BM = wide::BM;
+  const int lane = threadIdx.x & 63;
+  const int C = (E + 63) >> 6;
+  const int first = lane * C;
+  int units = 0;
+  for (int i = 0; i < C; ++i) {
+    const int e = first + i;
+    if (e < E) units += units_of<BM>(off[e + 1] - off[e]);
+  }
+  int incl = units;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  const int excl = incl - units;
+  const int64_t total = (int64_t)__shfl(incl, 63) * ntiles;
+  const int64_t w = x * total / 8 + j;
+  e_out = -1;
+  n_out = loc_out = 0;
+  if (w >= (x + 1) * total / 8) return;
+  const int p = (int)(w / ntiles);  // a unit of the wanted expert
+  const bool mine = p >= excl && p < incl;
+  const unsigned long long msk = __ballot(mine);
+  if (msk == 0) return;
+  const int src = __ffsll((long long)msk) - 1;
+  int ee = -1, ue = 0, ke = 1;
+  if (mine) {
+    int acc = excl;
+    for (int i = 0; i < C; ++i) {
+      const int e = first + i;
+      if (e < E) {
+        const int n = units_of<BM>(off[e + 1] - off[e]);
+        if (p < acc + n) {
+          ee = e;
+          ue = acc;
+          ke = n;
+          break;
+        }
+        acc += n;
+      }
+    }
+  }
+  ee = __shfl(ee, src);
+  ue = __shfl(ue, src);
+  ke = __shfl(ke, src);
+  const int64_t local = w - (int64_t)ue * ntiles;
+  e_out = ee;
+  n_out = (int)(local / ke);
+  loc_out = (int)(local % ke);
+}
+
 // NST > 0: K / 256 is a compile-time constant and the ring is fully unrolled;
 // NST == 0: any K (multiple of 256) with a runtime loop.
 template <int kMode, bool kYBF16, int NST>
@@ -48,24 +113,31 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;  // rows [64 wm, 64 wm + 64), column half wn
 
-  // XCD-aware order (block b runs on XCD b % 8): XCD x owns n-tiles [x*nt/8, (x+1)*nt/8)
   const int ntiles = a.ntiles;
   const int x = (int)(blockIdx.x & 7u), jb = (int)(blockIdx.x >> 3);
-  const int n_lo = x * ntiles / 8, n_hi = (x + 1) * ntiles / 8, nn = n_hi - n_lo;
-  if (nn == 0) return;
-  const int m_unit = jb / nn;
-  const int n_tile = n_lo + jb % nn;
-
-  int e = 0;
+  int e = 0, n_tile;
   int64_t row0;
   int m;
-  if (kMode == kModeDense) {
-    row0 = (int64_t)m_unit * BM;
-    if (row0 >= a.M) return;
-    m = (int)(a.M - row0 < BM ? a.M - row0 : BM);
+  if (kMode == kModeDense || !MXF_WIDE_ORDER) {
+    // XCD x owns n-tiles [x*nt/8, (x+1)*nt/8) and walks the row units
+    const int n_lo = x * ntiles / 8, n_hi = (x + 1) * ntiles / 8, nn = n_hi - n_lo;
+    if (nn == 0) return;
+    const int m_unit = jb / nn;
+    n_tile = n_lo + jb % nn;
+    if (kMode == kModeDense) {
+      row0 = (int64_t)m_unit * BM;
+      if (row0 >= a.M) return;
+      m = (int)(a.M - row0 < BM ? a.M - row0 : BM);
+    } else {
+      int loc;
+      find_unit<BM>(a.offsets, a.E, m_unit, e, loc);
+      if (e < 0) return;
+      row0 = a.offsets[e] + (int64_t)loc * BM;
+      m = min(BM, a.offsets[e + 1] - (int)row0);
+    }
   } else {
     int loc;
-    find_unit<BM>(a.offsets, a.E, m_unit, e, loc);
+    wide_work_item(a.offsets, a.E, ntiles, x, jb, e, n_tile, loc);
     if (e < 0) return;
     row0 = a.offsets[e] + (int64_t)loc * BM;
     m = min(BM, a.offsets[e + 1] - (int)row0);

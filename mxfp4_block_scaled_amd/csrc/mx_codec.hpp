@@ -31,25 +31,23 @@ __device__ __forceinline__ float inv_scale_from_byte(uint32_t byte) {
   return __uint_as_float((254u - byte) << 23);
 }
 
-// |t| -> 7-bit E4M3 magnitude code (0x00 .. 0x7E)
+// |t| -> 7-bit E4M3 magnitude code (0x00 .. 0x7E). Every case is computed and the
+// right one selected, so a wave runs no branches per element.
 __device__ __forceinline__ uint32_t e4m3_mag_code(float a) {
-  if (a >= 448.0f) return 0x7Eu;
-  if (a < 0.015625f) {  // below 2^-6: subnormal grid m * 2^-9, m = 0..8 (8 = 2^-6)
-    return (uint32_t)__builtin_rintf(a * 512.0f);
-  }
-  uint32_t u = __float_as_uint(a);
-  uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;  // (exp << 3 | m3), rounded
-  return r - ((127u - 7u) << 3);
+  // below 2^-6: subnormal grid m * 2^-9, m = 0..8 (8 = 2^-6)
+  const uint32_t sub = (uint32_t)__builtin_rintf(fminf(a, 0.015625f) * 512.0f);
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t nrm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);  // (exp << 3 | m3), rounded
+  return a >= 448.0f ? 0x7Eu : (a < 0.015625f ? sub : nrm);
 }
 
-// |t| -> 3-bit E2M1 magnitude code (0 .. 7)
+// |t| -> 3-bit E2M1 magnitude code (0 .. 7), branch-free like e4m3_mag_code
 __device__ __forceinline__ uint32_t e2m1_mag_code(float a) {
-  if (a >= 6.0f) return 7u;
-  if (a < 1.0f) return (uint32_t)__builtin_rintf(a * 2.0f);  // 0, 0.5, 1.0
-  uint32_t u = __float_as_uint(a);
-  uint32_t r = (u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22;  // (exp << 1 | m1), rounded
-  uint32_t c = r - ((127u - 1u) << 1);
-  return c > 7u ? 7u : c;
+  const uint32_t sub = (uint32_t)__builtin_rintf(fminf(a, 1.0f) * 2.0f);  // 0, 0.5, 1.0 below 1
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t r = (u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22;  // (exp << 1 | m1), rounded
+  const uint32_t nrm = min(r - ((127u - 1u) << 1), 7u);
+  return a >= 6.0f ? 7u : (a < 1.0f ? sub : nrm);
 }
 
 __device__ __forceinline__ uint32_t e4m3_code(float v, float inv_scale) {
