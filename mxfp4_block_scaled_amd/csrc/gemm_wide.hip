@@ -103,6 +103,89 @@ __device__ __forceinline__ void wide_work_item(const int32_t* __restrict__ off, 
   loc_out = (int)(local % ke);
 }
 
+// Epilogue of one 256 x 256 tile: wave (wm, wn) writes its 64 x 128 block through
+// its own LDS staging region stg (8704 bytes). FC1: h = silu(gate) * up,
+// requantised per 32 along I; FC2 / dense: y or c in bf16 or fp32.
+template <int kMode, bool kYBF16>
+__device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&acc)[2][4], uint8_t* stg, int n_tile,
+                                              int64_t row0, int m) {
+  using namespace wide;
+  auto lds_wave_fence = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5, r32 = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+  if (64 * wm >= m) return;
+  if (kMode == kModeFC1) {
+    // h = silu(gate) * up for 32 rows x 64 I-columns at a time (two quantisation
+    // blocks per row); lane l requantises block l % 2 of row l / 2
+    float(*hf)[68] = reinterpret_cast<float(*)[68]>(stg);
+    const int64_t icol = (int64_t)n_tile * (BN / 2) + 64 * wn;
+    const int64_t hrow = a.I / 2;
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          hf[8 * (v >> 2) + 4 * g + (v & 3)][32 * f + r32] = silu_mul(acc[fm][f][v], acc[fm][f + 2][v]);
+      lds_wave_fence();
+      const int lr = 64 * wm + 32 * fm + (lane >> 1), blk = lane & 1;
+      if (lr < m) {
+        const int64_t Rw = row0 + lr;
+        quantize_store32<true>(&hf[lane >> 1][32 * blk], a.h + Rw * hrow + (icol + 32 * blk) / 2,
+                               a.h_scale + Rw * (a.I / 32) + (icol + 32 * blk) / 32);
+      }
+      lds_wave_fence();
+    }
+  } else if (kYBF16) {
+    uint16_t(*ob)[136] = reinterpret_cast<uint16_t(*)[136]>(stg);  // 32 x 136 x 2 = 8704 bytes
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    const int64_t col0 = (int64_t)n_tile * BN + 128 * wn;
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) {
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          ob[8 * (v >> 2) + 4 * g + (v & 3)][32 * fn + r32] = (uint16_t)bf16_round(acc[fm][fn][v]);
+      lds_wave_fence();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {  // 32 rows x 128 columns = 512 pieces of 16 bytes
+        const int idx = lane + 64 * j;
+        const int rr = idx >> 4, c8 = idx & 15;
+        const int lr = 64 * wm + 32 * fm + rr;
+        if (lr < m)
+          *reinterpret_cast<uint4*>(out + (row0 + lr) * a.N + col0 + 8 * c8) =
+              *reinterpret_cast<const uint4*>(&ob[rr][8 * c8]);
+      }
+      lds_wave_fence();
+    }
+  } else {
+    float(*of)[68] = reinterpret_cast<float(*)[68]>(stg);  // 32 x 68 x 4 = 8704 bytes
+    float* out = static_cast<float*>(a.out);
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {  // column fragments 2 p, 2 p + 1
+        const int64_t col0 = (int64_t)n_tile * BN + 128 * wn + 64 * p;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) of[8 * (v >> 2) + 4 * g + (v & 3)][32 * h + r32] = acc[fm][2 * p + h][v];
+        lds_wave_fence();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {  // 32 rows x 64 columns = 512 pieces of 16 bytes
+          const int idx = lane + 64 * j;
+          const int rr = idx >> 4, c4 = idx & 15;
+          const int lr = 64 * wm + 32 * fm + rr;
+          if (lr < m)
+            *reinterpret_cast<float4*>(out + (row0 + lr) * a.N + col0 + 4 * c4) =
+                *reinterpret_cast<const float4*>(&of[rr][4 * c4]);
+        }
+        lds_wave_fence();
+      }
+  }
+}
+
 // NST > 0: K / 256 is a compile-time constant and the ring is fully unrolled;
 // NST == 0: any K (multiple of 256) with a runtime loop.
 template <int kMode, bool kYBF16, int NST>
@@ -217,16 +300,27 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
   struct Frags {
     v4i a[2], b[4];
   };
+  // Byte offset of a fragment row's chunk 4 g + s in a slot: the row's offset with
+  // chunk 4 g, XOR 16 s (s only touches bits 4-5). The offsets at s = 0 pass through
+  // an empty asm at every use, so the compiler recomputes the XOR per step instead
+  // of keeping one address register per (slot, step, fragment).
+  int aoff[2], boff[4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) aoff[f] = arow_l[f] * R + 16 * ((4 * g) ^ swz<CH>(arow_l[f]));
+#pragma unroll
+  for (int f = 0; f < 4; ++f) boff[f] = brow_l[f] * R + 16 * ((4 * g) ^ swz<CH>(brow_l[f]));
   auto load_frags = [&](const WideSlot& sl, int s, Frags& F) {
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-      const int r = arow_l[f];
-      F.a[f] = *reinterpret_cast<const v4i*>(&sl.A[r * R + 16 * ((4 * g + s) ^ swz<CH>(r))]);
+      int o = aoff[f];
+      asm volatile("" : "+v"(o));
+      F.a[f] = *reinterpret_cast<const v4i*>(&sl.A[o ^ (16 * s)]);
     }
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const int r = brow_l[f];
-      F.b[f] = *reinterpret_cast<const v4i*>(&sl.B[r * R + 16 * ((4 * g + s) ^ swz<CH>(r))]);
+      int o = boff[f];
+      asm volatile("" : "+v"(o));
+      F.b[f] = *reinterpret_cast<const v4i*>(&sl.B[o ^ (16 * s)]);
     }
   };
   auto mfma_step = [&](auto S_, const Frags& F, const int* sa, const int* sb) {
@@ -309,79 +403,8 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
 
   // wave w stages in slot0 (w < 4) or slot1 (w >= 4), region (w % 4) x STG bytes;
   // the staging writes and reads are this wave's own
-  uint8_t* const stg = (wave < 4 ? slot0.A : slot1.A) + (wave & 3) * STG;
-  auto lds_wave_fence = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
-  if (64 * wm >= m) return;
-  if (kMode == kModeFC1) {
-    // h = silu(gate) * up for 32 rows x 64 I-columns at a time (two quantisation
-    // blocks per row); lane l requantises block l % 2 of row l / 2
-    float(*hf)[68] = reinterpret_cast<float(*)[68]>(stg);
-    const int64_t icol = (int64_t)n_tile * (BN / 2) + 64 * wn;
-    const int64_t hrow = a.I / 2;
-#pragma unroll
-    for (int fm = 0; fm < 2; ++fm) {
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          hf[8 * (v >> 2) + 4 * g + (v & 3)][32 * f + r32] = silu_mul(acc[fm][f][v], acc[fm][f + 2][v]);
-      lds_wave_fence();
-      const int lr = 64 * wm + 32 * fm + (lane >> 1), blk = lane & 1;
-      if (lr < m) {
-        const int64_t Rw = row0 + lr;
-        quantize_store32<true>(&hf[lane >> 1][32 * blk], a.h + Rw * hrow + (icol + 32 * blk) / 2,
-                               a.h_scale + Rw * (a.I / 32) + (icol + 32 * blk) / 32);
-      }
-      lds_wave_fence();
-    }
-  } else if (kYBF16) {
-    uint16_t(*ob)[136] = reinterpret_cast<uint16_t(*)[136]>(stg);  // 32 x 136 x 2 = 8704 bytes
-    uint16_t* out = static_cast<uint16_t*>(a.out);
-    const int64_t col0 = (int64_t)n_tile * BN + 128 * wn;
-#pragma unroll
-    for (int fm = 0; fm < 2; ++fm) {
-#pragma unroll
-      for (int fn = 0; fn < 4; ++fn)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          ob[8 * (v >> 2) + 4 * g + (v & 3)][32 * fn + r32] = (uint16_t)bf16_round(acc[fm][fn][v]);
-      lds_wave_fence();
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {  // 32 rows x 128 columns = 512 pieces of 16 bytes
-        const int idx = lane + 64 * j;
-        const int rr = idx >> 4, c8 = idx & 15;
-        const int lr = 64 * wm + 32 * fm + rr;
-        if (lr < m)
-          *reinterpret_cast<uint4*>(out + (row0 + lr) * a.N + col0 + 8 * c8) =
-              *reinterpret_cast<const uint4*>(&ob[rr][8 * c8]);
-      }
-      lds_wave_fence();
-    }
-  } else {
-    float(*of)[68] = reinterpret_cast<float(*)[68]>(stg);  // 32 x 68 x 4 = 8704 bytes
-    float* out = static_cast<float*>(a.out);
-#pragma unroll
-    for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {  // column fragments 2 p, 2 p + 1
-        const int64_t col0 = (int64_t)n_tile * BN + 128 * wn + 64 * p;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) of[8 * (v >> 2) + 4 * g + (v & 3)][32 * h + r32] = acc[fm][2 * p + h][v];
-        lds_wave_fence();
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {  // 32 rows x 64 columns = 512 pieces of 16 bytes
-          const int idx = lane + 64 * j;
-          const int rr = idx >> 4, c4 = idx & 15;
-          const int lr = 64 * wm + 32 * fm + rr;
-          if (lr < m)
-            *reinterpret_cast<float4*>(out + (row0 + lr) * a.N + col0 + 4 * c4) =
-                *reinterpret_cast<const float4*>(&of[rr][4 * c4]);
-        }
-        lds_wave_fence();
-      }
-  }
+  wide_epilogue<kMode, kYBF16>(a, acc, reinterpret_cast<uint8_t*>(wave < 4 ? &slot0 : &slot1) + (wave & 3) * STG, n_tile,
+                               row0, m);
 }
 
 template <int kMode, bool kYBF16>
