@@ -47,7 +47,7 @@ TRAFFIC_SRC_SHA256 = "6e0a2f597f4f615e87b6704e145ebb34ed209bb6d4b8c4e3c98842d68c
 TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8254209638, "moe_decode_t8": 1019645952}
 
 
-GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip")
+GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "mx_codec.hpp")
 
 
 def gemm_sources_sha256():

@@ -26,7 +26,7 @@ constexpr int SB = KS / 32;              // scale bytes per row per stage
 constexpr int IA = BM * CH / 64 / 8;     // A copies (16 B per lane) per wave per stage
 constexpr int IB = BN * CH / 64 / 8;     // B copies per wave per stage
 constexpr int D = IA + IB + 2;           // + one A-scale and one B-scale copy (4 B per lane)
-constexpr int STG = 8704;                // epilogue staging bytes per wave
+constexpr int STG = 8704;                // FC2 / dense epilogue staging bytes per wave
 }  // namespace wide
 
 struct alignas(16) WideSlot {
@@ -103,86 +103,119 @@ __device__ __forceinline__ void wide_work_item(const int32_t* __restrict__ off, 
   loc_out = (int)(local % ke);
 }
 
-// Epilogue of one 256 x 256 tile: wave (wm, wn) writes its 64 x 128 block through
-// its own LDS staging region stg (8704 bytes). FC1: h = silu(gate) * up,
-// requantised per 32 along I; FC2 / dense: y or c in bf16 or fp32.
+// Epilogue of one 256 x 256 tile, straight from the accumulators (no LDS). The
+// MFMAs take the weight fragment as their first operand, so acc[fm][fn][v] of
+// lane l is token row 64 wm + 32 fm + l % 32 and output column c(fn) + 8 (v / 4)
+// + 4 (l / 32) + v % 4: every lane holds runs of 4 consecutive columns of one row.
+// FC1: h = silu(gate) * up, requantised to E2M1 per 32 I-columns - a block is one
+// fragment's 32 columns of one row, held half by lane l and half by lane l ^ 32;
+// FC2 / dense: y or c in bf16 or fp32, staged per 32 rows in the wave's LDS region
+// stg (8-byte runs in, 16-byte row pieces out, so each store instruction writes
+// whole 256- or 512-byte row segments).
 template <int kMode, bool kYBF16>
 __device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&acc)[2][4], uint8_t* stg, int n_tile,
                                               int64_t row0, int m) {
   using namespace wide;
-  auto lds_wave_fence = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5, r32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;
   if (64 * wm >= m) return;
-  if (kMode == kModeFC1) {
-    // h = silu(gate) * up for 32 rows x 64 I-columns at a time (two quantisation
-    // blocks per row); lane l requantises block l % 2 of row l / 2
-    float(*hf)[68] = reinterpret_cast<float(*)[68]>(stg);
-    const int64_t icol = (int64_t)n_tile * (BN / 2) + 64 * wn;
-    const int64_t hrow = a.I / 2;
 #pragma unroll
-    for (int fm = 0; fm < 2; ++fm) {
+  for (int fm = 0; fm < 2; ++fm) {
+    const int lr = 64 * wm + 32 * fm + r32;
+    const bool ok = lr < m;
+    const int64_t Rw = row0 + lr;
+    if (kMode == kModeFC1) {
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < 2; ++f) {  // gate fragment f, up fragment f + 2: I-columns icol + [0, 32)
+        float h[16];
+        uint32_t amax = 0;
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          hf[8 * (v >> 2) + 4 * g + (v & 3)][32 * f + r32] = silu_mul(acc[fm][f][v], acc[fm][f + 2][v]);
-      lds_wave_fence();
-      const int lr = 64 * wm + 32 * fm + (lane >> 1), blk = lane & 1;
-      if (lr < m) {
-        const int64_t Rw = row0 + lr;
-        quantize_store32<true>(&hf[lane >> 1][32 * blk], a.h + Rw * hrow + (icol + 32 * blk) / 2,
-                               a.h_scale + Rw * (a.I / 32) + (icol + 32 * blk) / 32);
+        for (int v = 0; v < 16; ++v) {
+          h[v] = silu_mul(acc[fm][f][v], acc[fm][f + 2][v]);
+          amax = max(amax, __float_as_uint(h[v]) & 0x7FFFFFFFu);
+        }
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+        const uint32_t byte = scale_byte_from_amax_bits(amax, kEmaxE2M1);
+        // E2M1 codes by the hardware conversion (equal to e2m1_code; small scale
+        // bytes lifted by 2^64 as in quantize_block32)
+        const bool lift = byte < 64u;
+        const float mul = lift ? 18446744073709551616.0f : 1.0f;
+        const float sc = __uint_as_float((byte + (lift ? 64u : 0u)) << 23);
+        uint32_t c[2];  // bytes 2 j, 2 j + 1 of c[j / 2 ... ]: the 4 codes of column run j
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float* x = &h[8 * q];
+          uint32_t w = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0] * mul, x[1] * mul, sc, 0);
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2] * mul, x[3] * mul, sc, 1);
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4] * mul, x[5] * mul, sc, 2);
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6] * mul, x[7] * mul, sc, 3);
+#endif
+          c[q] = w;
+        }
+        const uint32_t p0 = (uint32_t)__shfl_xor((int)c[0], 32), p1 = (uint32_t)__shfl_xor((int)c[1], 32);
+        // the block's 16 bytes: 2-byte runs in column order, lane g = 0's run j, then lane 1's
+        if (g == 0 && ok) {
+          const int64_t icol = (int64_t)n_tile * (BN / 2) + 64 * wn + 32 * f;
+          const uint4 d = make_uint4((c[0] & 0xFFFFu) | (p0 << 16), (c[0] >> 16) | (p0 & 0xFFFF0000u),
+                                     (c[1] & 0xFFFFu) | (p1 << 16), (c[1] >> 16) | (p1 & 0xFFFF0000u));
+          *reinterpret_cast<uint4*>(a.h + Rw * (a.I / 2) + icol / 2) = d;
+          a.h_scale[Rw * (a.I / 32) + icol / 32] = (uint8_t)byte;
+        }
       }
-      lds_wave_fence();
-    }
-  } else if (kYBF16) {
-    uint16_t(*ob)[136] = reinterpret_cast<uint16_t(*)[136]>(stg);  // 32 x 136 x 2 = 8704 bytes
-    uint16_t* out = static_cast<uint16_t*>(a.out);
-    const int64_t col0 = (int64_t)n_tile * BN + 128 * wn;
-#pragma unroll
-    for (int fm = 0; fm < 2; ++fm) {
+    } else if (kYBF16) {
+      uint16_t(*ob)[136] = reinterpret_cast<uint16_t(*)[136]>(stg);  // 32 x 136 x 2 = 8704 bytes
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          ob[8 * (v >> 2) + 4 * g + (v & 3)][32 * fn + r32] = (uint16_t)bf16_round(acc[fm][fn][v]);
-      lds_wave_fence();
+        for (int j = 0; j < 4; ++j) {
+          const __bf16 b0 = (__bf16)acc[fm][fn][4 * j], b1 = (__bf16)acc[fm][fn][4 * j + 1];
+          const __bf16 b2 = (__bf16)acc[fm][fn][4 * j + 2], b3 = (__bf16)acc[fm][fn][4 * j + 3];
+          uint2 d;
+          d.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+          d.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+          *reinterpret_cast<uint2*>(&ob[r32][32 * fn + 8 * j + 4 * g]) = d;
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      uint16_t* out = static_cast<uint16_t*>(a.out);
+      const int64_t col0 = (int64_t)n_tile * BN + 128 * wn;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {  // 32 rows x 128 columns = 512 pieces of 16 bytes
         const int idx = lane + 64 * j;
         const int rr = idx >> 4, c8 = idx & 15;
-        const int lr = 64 * wm + 32 * fm + rr;
-        if (lr < m)
-          *reinterpret_cast<uint4*>(out + (row0 + lr) * a.N + col0 + 8 * c8) =
+        if (64 * wm + 32 * fm + rr < m)
+          *reinterpret_cast<uint4*>(out + (row0 + 64 * wm + 32 * fm + rr) * a.N + col0 + 8 * c8) =
               *reinterpret_cast<const uint4*>(&ob[rr][8 * c8]);
       }
-      lds_wave_fence();
-    }
-  } else {
-    float(*of)[68] = reinterpret_cast<float(*)[68]>(stg);  // 32 x 68 x 4 = 8704 bytes
-    float* out = static_cast<float*>(a.out);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    } else {
+      float(*of)[132] = reinterpret_cast<float(*)[132]>(stg);  // 16 x 132 x 4 = 8448 bytes
+      float* out = static_cast<float*>(a.out);
+      const int64_t col0 = (int64_t)n_tile * BN + 128 * wn;
 #pragma unroll
-    for (int fm = 0; fm < 2; ++fm)
+      for (int hh = 0; hh < 2; ++hh) {  // rows r32 in [16 hh, 16 hh + 16)
+        if ((r32 >> 4) == hh) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {  // column fragments 2 p, 2 p + 1
-        const int64_t col0 = (int64_t)n_tile * BN + 128 * wn + 64 * p;
+          for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+            for (int j = 0; j < 4; ++j)
+              *reinterpret_cast<float4*>(&of[r32 & 15][32 * fn + 8 * j + 4 * g]) =
+                  make_float4(acc[fm][fn][4 * j], acc[fm][fn][4 * j + 1], acc[fm][fn][4 * j + 2], acc[fm][fn][4 * j + 3]);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-          for (int v = 0; v < 16; ++v) of[8 * (v >> 2) + 4 * g + (v & 3)][32 * h + r32] = acc[fm][2 * p + h][v];
-        lds_wave_fence();
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {  // 32 rows x 64 columns = 512 pieces of 16 bytes
+        for (int j = 0; j < 8; ++j) {  // 16 rows x 128 columns = 512 pieces of 16 bytes
           const int idx = lane + 64 * j;
-          const int rr = idx >> 4, c4 = idx & 15;
-          const int lr = 64 * wm + 32 * fm + rr;
-          if (lr < m)
-            *reinterpret_cast<float4*>(out + (row0 + lr) * a.N + col0 + 4 * c4) =
+          const int rr = idx >> 5, c4 = idx & 31;
+          const int lrow = 64 * wm + 32 * fm + 16 * hh + rr;
+          if (lrow < m)
+            *reinterpret_cast<float4*>(out + (row0 + lrow) * a.N + col0 + 4 * c4) =
                 *reinterpret_cast<const float4*>(&of[rr][4 * c4]);
         }
-        lds_wave_fence();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
+    }
   }
 }
 
@@ -331,7 +364,7 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn) {
         const v8i bf = v8i{F.b[fn][0], F.b[fn][1], F.b[fn][2], F.b[fn][3], 0, 0, 0, 0};
-        acc[fm][fn] = mfma32x32x64<kFmtFP4, kFmtFP4, s>(af, bf, acc[fm][fn], sa[fm], sb[fn]);
+        acc[fm][fn] = mfma32x32x64<kFmtFP4, kFmtFP4, s>(bf, af, acc[fm][fn], sb[fn], sa[fm]);
       }
     }
   };
@@ -399,12 +432,9 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
   for (int j = 0; j < D; ++j) issue_one(slot0, 0, j);
   if (64 * wm < __builtin_amdgcn_readfirstlane(m)) run(std::true_type{});
   else run(std::false_type{});
-  lds_barrier();  // every wave is done reading the ring; the slots become staging areas
-
-  // wave w stages in slot0 (w < 4) or slot1 (w >= 4), region (w % 4) x STG bytes;
-  // the staging writes and reads are this wave's own
-  wide_epilogue<kMode, kYBF16>(a, acc, reinterpret_cast<uint8_t*>(wave < 4 ? &slot0 : &slot1) + (wave & 3) * STG, n_tile,
-                               row0, m);
+  if (kMode != kModeFC1) lds_barrier();  // every wave is done reading the ring: its slots become staging
+  wide_epilogue<kMode, kYBF16>(a, acc, reinterpret_cast<uint8_t*>(wave < 4 ? &slot0 : &slot1) + (wave & 3) * STG,
+                               n_tile, row0, m);
 }
 
 template <int kMode, bool kYBF16>

@@ -71,6 +71,27 @@ __device__ __forceinline__ uint32_t quantize_block32(const float (&v)[32], uint3
   const uint32_t byte = scale_byte_from_amax_bits(amax, kFP4 ? kEmaxE2M1 : kEmaxE4M3);
   const float inv = inv_scale_from_byte(byte);
   if (kFP4) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // gfx950's scaled E2M1 conversion (v / scale, round to nearest even on the E2M1
+    // grid, saturating, sign kept) gives exactly e2m1_code(v, 1 / scale): checked on
+    // the GPU for every finite bf16 pattern, a million random fp32 values and the
+    // grid midpoints with their neighbours, scale bytes 117..137. Blocks with a scale
+    // byte below 64 are lifted by 2^64 (values and scale alike, exact) so that the
+    // scale operand and the elements stay normal fp32 numbers.
+    const bool lift = byte < 64u;
+    const float mul = lift ? 18446744073709551616.0f : 1.0f;
+    const float sc = __uint_as_float((byte + (lift ? 64u : 0u)) << 23);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* x = &v[w * 8];
+      uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[0] * mul, x[1] * mul, sc, 0);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, x[2] * mul, x[3] * mul, sc, 1);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, x[4] * mul, x[5] * mul, sc, 2);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, x[6] * mul, x[7] * mul, sc, 3);
+      out[w] = word;
+    }
+    (void)inv;
+#else
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       uint32_t word = 0;
@@ -78,6 +99,7 @@ __device__ __forceinline__ uint32_t quantize_block32(const float (&v)[32], uint3
       for (int n = 0; n < 8; ++n) word |= e2m1_code(v[w * 8 + n], inv) << (4 * n);
       out[w] = word;
     }
+#endif
   } else {
 #pragma unroll
     for (int w = 0; w < 8; ++w) {

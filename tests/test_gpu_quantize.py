@@ -63,6 +63,28 @@ def test_quantize_fp32_input_bit_exact(fmt):
     assert np.array_equal(host(q), ref_q)
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_quantize_small_scale_bytes_bit_exact(fmt):
+    """Blocks whose scale byte is 0 .. 80 (amax down to fp32 subnormals): grid
+    midpoints and their fp32 neighbours, so every rounding decision of the
+    smallest scales is checked."""
+    g = np.random.default_rng(9)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0], np.float64)
+    rows = []
+    for e in range(-149, -41, 3):  # 36 blocks
+        base = np.resize(mids, 32) * 2.0 ** e
+        v = base.astype(np.float32)
+        v = np.where(g.random(32) < 0.33, np.nextafter(v, np.float32(np.inf)), v)
+        v = np.where(g.random(32) < 0.33, np.nextafter(v, np.float32(0)), v)
+        rows.append(v * g.choice(np.array([-1.0, 1.0], np.float32), 32))
+    x = np.concatenate(rows).astype(np.float32).reshape(-1, 128)
+    q, qs = ops.mxfp4_quantize_act(torch.from_numpy(x).cuda(), fmt)
+    ref_q, ref_s = oracle.moe.quantize_act(x.astype(np.float64), fmt)
+    assert ref_s.min() == 0 and ref_s.max() >= 64
+    assert np.array_equal(host(qs), ref_s)
+    assert np.array_equal(host(q), ref_q)
+
+
 @pytest.mark.parametrize("name", ["moe_decode_t8", "moe_prefill_t2048_zipf", "moe_prefill_t16384_fp4"])
 def test_quantize_layer_inputs_bit_exact(name):
     d = dg.workload_inputs(name, weights=False)
