@@ -23,19 +23,24 @@ constexpr int S = KS / 64;               // MFMA steps per stage
 constexpr int R = KS / 2;                // bytes per row per stage (E2M1, A and B alike)
 constexpr int CH = R / 16;               // 16-byte chunks per row
 constexpr int SB = KS / 32;              // scale bytes per row per stage
+constexpr int G = 4;                     // stages per scale group
+constexpr int SG = G * SB;               // scale bytes per row per group
 constexpr int IA = BM * CH / 64 / 8;     // A copies (16 B per lane) per wave per stage
 constexpr int IB = BN * CH / 64 / 8;     // B copies per wave per stage
-constexpr int D = IA + IB + 2;           // + one A-scale and one B-scale copy (4 B per lane)
+constexpr int D = IA + IB;
 constexpr int STG = 8704;                // FC2 / dense epilogue staging bytes per wave
 }  // namespace wide
 
 struct alignas(16) WideSlot {
   uint8_t A[wide::BM * wide::R];
   uint8_t B[wide::BN * wide::R];
-  uint8_t As[wide::BM * wide::SB];
-  uint8_t Bs[wide::BN * wide::SB];
 };
-static_assert(2 * sizeof(WideSlot) <= 160 * 1024, "two ring slots must fit in LDS");
+// the scales of G stages ([256 rows][32 bytes] per operand), double-buffered
+struct alignas(16) WideScales {
+  uint8_t A[wide::BM * wide::SG];
+  uint8_t B[wide::BN * wide::SG];
+};
+static_assert(2 * sizeof(WideSlot) + 2 * sizeof(WideScales) <= 160 * 1024, "ring and scale buffers must fit in LDS");
 static_assert(4 * wide::STG <= (int)sizeof(WideSlot), "four waves' staging regions must fit a slot");
 
 #ifndef MXF_WIDE_ORDER
@@ -224,6 +229,9 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&ac
 template <int kMode, bool kYBF16, int NST>
 __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
   using namespace wide;
+  // the scale buffers first: at LDS addresses below 64 KB their offsets fit an
+  // LDS instruction's immediate field
+  __shared__ WideScales scl0, scl1;
   __shared__ WideSlot slot0, slot1;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
@@ -294,22 +302,26 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
     const int r = chunk / CH, pc = chunk % CH;
     vb[q] = (uint32_t)(b_row(r) * wrow + 16 * (pc ^ swz<CH>(r)));
   }
-  // scale copies in 4-byte pieces, lane l's piece landing at 4 l: wave w fills rows
-  // [32 w, 32 w + 32) of the [256][8] A-scale and B-scale slots
-  const uint32_t vsa = (uint32_t)(a_src_row(32 * wave + (lane >> 1)) * srow + 4 * (lane & 1));
-  const uint32_t vsb = (uint32_t)(b_row(32 * wave + (lane >> 1)) * srow + 4 * (lane & 1));
+  // Scales move in groups of G stages (32 bytes per row): one 16-byte piece per
+  // lane, lane l's piece landing at 16 l, so wave w fills rows [32 w, 32 w + 32) of
+  // a [256][32] group buffer with one copy per operand - a quarter of the copy
+  // instructions (each touching 32 rows) that per-stage scale copies would take.
+  // A group past the end of K reads other rows' bytes or, at the end of the
+  // buffer, zeros (range check); those bytes are never used.
+  const uint32_t vsa = (uint32_t)(a_src_row(32 * wave + (lane >> 1)) * srow + 16 * (lane & 1));
+  const uint32_t vsb = (uint32_t)(b_row(32 * wave + (lane >> 1)) * srow + 16 * (lane & 1));
+  auto issue_scales = [&](WideScales& sc, int grp) {
+    buf_dma16(ras, &sc.A[wave * 1024], vsa, (uint32_t)grp * SG);
+    buf_dma16(rbs, &sc.B[wave * 1024], vsb, (uint32_t)grp * SG);
+  };
 
-  // copy j (0 .. D-1) of stage st into slot sl: A chunks, B chunks, A scales, B scales
+  // copy j (0 .. D-1) of stage st into slot sl: A chunks, then B chunks
   auto issue_one = [&](WideSlot& sl, int st, int j) {
     if (j < IA) {
       buf_dma16(ra, &sl.A[(wave * IA + j) * 1024], va[j], (uint32_t)st * R);
-    } else if (j < IA + IB) {
+    } else {
       const int q = j - IA;
       buf_dma16(rb, &sl.B[(wave * IB + q) * 1024], vb[q], (uint32_t)st * R);
-    } else if (j == IA + IB) {
-      buf_dma4(ras, &sl.As[wave * 256], vsa, (uint32_t)st * SB);
-    } else {
-      buf_dma4(rbs, &sl.Bs[wave * 256], vsb, (uint32_t)st * SB);
     }
   };
 
@@ -372,17 +384,28 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
   // One stage. Step s issues copies [s DC, (s + 1) DC) of stage nst_ into slot nsl
   // (when `more`), reads the fragments of step s + 1 and runs the MFMAs of step s;
   // full scheduling fences between the steps keep that order, so the copies spread
-  // over the stage and each step's LDS reads overlap the previous step's MFMAs.
+  // over the stage and each step's LDS reads overlap the previous step's MFMAs. The
+  // stage's scales are stage `sub` of group buffer csc; the last step also copies
+  // the next scale group into nsc (when `more_sc`).
   constexpr int DC = (D + S - 1) / S;
-  auto stage = [&](auto kActive, const WideSlot& sl, WideSlot& nsl, bool more, int nst_) {
+  auto stage = [&](auto kActive, const WideSlot& sl, WideSlot& nsl, bool more, int nst_, const WideScales& csc,
+                   WideScales& nsc, bool more_sc, int grp_next, int sub) {
     constexpr bool act = decltype(kActive)::value;
     int sa[2], sb[4];
     Frags F[2];
     if constexpr (act) {
 #pragma unroll
-      for (int f = 0; f < 2; ++f) sa[f] = *reinterpret_cast<const int*>(&sl.As[arow_l[f] * SB + 4 * g]);
+      for (int f = 0; f < 2; ++f) {
+        int o = arow_l[f] * SG + 4 * g;
+        asm volatile("" : "+v"(o));
+        sa[f] = *reinterpret_cast<const int*>(&csc.A[o + SB * sub]);
+      }
 #pragma unroll
-      for (int f = 0; f < 4; ++f) sb[f] = *reinterpret_cast<const int*>(&sl.Bs[brow_l[f] * SB + 4 * g]);
+      for (int f = 0; f < 4; ++f) {
+        int o = brow_l[f] * SG + 4 * g;
+        asm volatile("" : "+v"(o));
+        sb[f] = *reinterpret_cast<const int*>(&csc.B[o + SB * sub]);
+      }
       load_frags(sl, 0, F[0]);
     }
     auto one = [&](auto S_) {
@@ -391,6 +414,7 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = s * DC; j < (s + 1) * DC && j < D; ++j) issue_one(nsl, nst_, j);
       }
+      if (s == S - 1 && more_sc) issue_scales(nsc, grp_next);
       if constexpr (act) {
         if constexpr (s + 1 < S) load_frags(sl, s + 1, F[(s + 1) & 1]);
         mfma_step(S_, F[s & 1], sa, sb);
@@ -415,7 +439,10 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
       lds_barrier();
       WideSlot& cur = i == 0 ? slot0 : slot1;
       WideSlot& nxt = i == 0 ? slot1 : slot0;
-      stage(kActive, cur, nxt, st + 1 < nst, st + 1);
+      const int grp = st / G;
+      WideScales& csc = (grp & 1) ? scl1 : scl0;
+      WideScales& nsc = (grp & 1) ? scl0 : scl1;
+      stage(kActive, cur, nxt, st + 1 < nst, st + 1, csc, nsc, st % G == 0 && (grp + 1) * G < nst, grp + 1, st % G);
     };
     auto turn = [&](int st0) {
       step(std::integral_constant<int, 0>{}, st0);
@@ -430,6 +457,7 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
   };
 #pragma unroll
   for (int j = 0; j < D; ++j) issue_one(slot0, 0, j);
+  issue_scales(scl0, 0);
   if (64 * wm < __builtin_amdgcn_readfirstlane(m)) run(std::true_type{});
   else run(std::false_type{});
   if (kMode != kModeFC1) lds_barrier();  // every wave is done reading the ring: its slots become staging
