@@ -35,6 +35,7 @@ struct GemmArgs {
   int topk, E;
   int ntiles;  // tile kernel: weight-row tiles per expert (1-D grid: block = m_unit * ntiles + n_tile)
   int kchunk;  // dense weight-streaming kernel: 512-k super-steps per grid.y slice (0: the whole K)
+  int ngroup;  // wide kernel, grouped GEMMs: consecutive n-tiles per workgroup (ntiles % ngroup == 0; 0: one)
 };
 
 // ---------------------------------------------------------------------------------

@@ -28,7 +28,7 @@ constexpr int SG = G * SB;               // scale bytes per row per group
 constexpr int IA = BM * CH / 64 / 8;     // A copies (16 B per lane) per wave per stage
 constexpr int IB = BN * CH / 64 / 8;     // B copies per wave per stage
 constexpr int D = IA + IB;
-constexpr int STG = 8704;                // FC2 / dense epilogue staging bytes per wave
+constexpr int STG = 4352;                // FC2 / dense epilogue staging bytes per wave
 }  // namespace wide
 
 struct alignas(16) WideSlot {
@@ -41,7 +41,7 @@ struct alignas(16) WideScales {
   uint8_t B[wide::BN * wide::SG];
 };
 static_assert(2 * sizeof(WideSlot) + 2 * sizeof(WideScales) <= 160 * 1024, "ring and scale buffers must fit in LDS");
-static_assert(4 * wide::STG <= (int)sizeof(WideSlot), "four waves' staging regions must fit a slot");
+static_assert(8 * wide::STG <= (int)sizeof(WideSlot), "eight waves' staging regions must fit one slot");
 
 #ifndef MXF_WIDE_ORDER
 #define MXF_WIDE_ORDER 1
@@ -114,9 +114,9 @@ __device__ __forceinline__ void wide_work_item(const int32_t* __restrict__ off, 
 // + 4 (l / 32) + v % 4: every lane holds runs of 4 consecutive columns of one row.
 // FC1: h = silu(gate) * up, requantised to E2M1 per 32 I-columns - a block is one
 // fragment's 32 columns of one row, held half by lane l and half by lane l ^ 32;
-// FC2 / dense: y or c in bf16 or fp32, staged per 32 rows in the wave's LDS region
-// stg (8-byte runs in, 16-byte row pieces out, so each store instruction writes
-// whole 256- or 512-byte row segments).
+// FC2 / dense: y or c in bf16 or fp32, staged 16 (bf16) or 8 (fp32) rows at a time
+// in the wave's 4352-byte LDS region stg (8- or 16-byte runs in, 16-byte row pieces
+// out, so each store instruction writes whole 256- or 512-byte row segments).
 template <int kMode, bool kYBF16>
 __device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&acc)[2][4], uint8_t* stg, int n_tile,
                                               int64_t row0, int m) {
@@ -170,33 +170,8 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&ac
         }
       }
     } else if (kYBF16) {
-      uint16_t(*ob)[136] = reinterpret_cast<uint16_t(*)[136]>(stg);  // 32 x 136 x 2 = 8704 bytes
-#pragma unroll
-      for (int fn = 0; fn < 4; ++fn)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const __bf16 b0 = (__bf16)acc[fm][fn][4 * j], b1 = (__bf16)acc[fm][fn][4 * j + 1];
-          const __bf16 b2 = (__bf16)acc[fm][fn][4 * j + 2], b3 = (__bf16)acc[fm][fn][4 * j + 3];
-          uint2 d;
-          d.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-          d.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-          *reinterpret_cast<uint2*>(&ob[r32][32 * fn + 8 * j + 4 * g]) = d;
-        }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      uint16_t(*ob)[136] = reinterpret_cast<uint16_t(*)[136]>(stg);  // 16 x 136 x 2 = 4352 bytes
       uint16_t* out = static_cast<uint16_t*>(a.out);
-      const int64_t col0 = (int64_t)n_tile * BN + 128 * wn;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {  // 32 rows x 128 columns = 512 pieces of 16 bytes
-        const int idx = lane + 64 * j;
-        const int rr = idx >> 4, c8 = idx & 15;
-        if (64 * wm + 32 * fm + rr < m)
-          *reinterpret_cast<uint4*>(out + (row0 + 64 * wm + 32 * fm + rr) * a.N + col0 + 8 * c8) =
-              *reinterpret_cast<const uint4*>(&ob[rr][8 * c8]);
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    } else {
-      float(*of)[132] = reinterpret_cast<float(*)[132]>(stg);  // 16 x 132 x 4 = 8448 bytes
-      float* out = static_cast<float*>(a.out);
       const int64_t col0 = (int64_t)n_tile * BN + 128 * wn;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {  // rows r32 in [16 hh, 16 hh + 16)
@@ -204,16 +179,47 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&ac
 #pragma unroll
           for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const __bf16 b0 = (__bf16)acc[fm][fn][4 * j], b1 = (__bf16)acc[fm][fn][4 * j + 1];
+              const __bf16 b2 = (__bf16)acc[fm][fn][4 * j + 2], b3 = (__bf16)acc[fm][fn][4 * j + 3];
+              uint2 d;
+              d.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+              d.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+              *reinterpret_cast<uint2*>(&ob[r32 & 15][32 * fn + 8 * j + 4 * g]) = d;
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // 16 rows x 128 columns = 256 pieces of 16 bytes
+          const int idx = lane + 64 * j;
+          const int rr = idx >> 4, c8 = idx & 15;
+          const int lrow = 64 * wm + 32 * fm + 16 * hh + rr;
+          if (lrow < m)
+            *reinterpret_cast<uint4*>(out + (row0 + lrow) * a.N + col0 + 8 * c8) =
+                *reinterpret_cast<const uint4*>(&ob[rr][8 * c8]);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+    } else {
+      float(*of)[132] = reinterpret_cast<float(*)[132]>(stg);  // 8 x 132 x 4 = 4224 bytes
+      float* out = static_cast<float*>(a.out);
+      const int64_t col0 = (int64_t)n_tile * BN + 128 * wn;
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {  // rows r32 in [8 hh, 8 hh + 8)
+        if ((r32 >> 3) == hh) {
+#pragma unroll
+          for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
             for (int j = 0; j < 4; ++j)
-              *reinterpret_cast<float4*>(&of[r32 & 15][32 * fn + 8 * j + 4 * g]) =
+              *reinterpret_cast<float4*>(&of[r32 & 7][32 * fn + 8 * j + 4 * g]) =
                   make_float4(acc[fm][fn][4 * j], acc[fm][fn][4 * j + 1], acc[fm][fn][4 * j + 2], acc[fm][fn][4 * j + 3]);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {  // 16 rows x 128 columns = 512 pieces of 16 bytes
+        for (int j = 0; j < 4; ++j) {  // 8 rows x 128 columns = 256 pieces of 16 bytes
           const int idx = lane + 64 * j;
           const int rr = idx >> 5, c4 = idx & 31;
-          const int lrow = 64 * wm + 32 * fm + 16 * hh + rr;
+          const int lrow = 64 * wm + 32 * fm + 8 * hh + rr;
           if (lrow < m)
             *reinterpret_cast<float4*>(out + (row0 + lrow) * a.N + col0 + 4 * c4) =
                 *reinterpret_cast<const float4*>(&of[rr][4 * c4]);
@@ -226,7 +232,17 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&ac
 
 // NST > 0: K / 256 is a compile-time constant and the ring is fully unrolled;
 // NST == 0: any K (multiple of 256) with a runtime loop.
-template <int kMode, bool kYBF16, int NST>
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// NTG: consecutive n-tiles per workgroup (grouped GEMMs in the expert-major order;
+// 1 for dense), unrolled like the stages
+template <int kMode, bool kYBF16, int NST, int NTG>
 __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
   using namespace wide;
   // the scale buffers first: at LDS addresses below 64 KB their offsets fit an
@@ -239,6 +255,8 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
 
   const int ntiles = a.ntiles;
   const int x = (int)(blockIdx.x & 7u), jb = (int)(blockIdx.x >> 3);
+  static_assert(NTG == 1 || (NST > 0 && NST % 2 == 0 && kMode != kModeDense), "n-tile groups need an even stage count");
+  constexpr int ntg = NTG;
   int e = 0, n_tile;
   int64_t row0;
   int m;
@@ -260,9 +278,10 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
       m = min(BM, a.offsets[e + 1] - (int)row0);
     }
   } else {
-    int loc;
-    wide_work_item(a.offsets, a.E, ntiles, x, jb, e, n_tile, loc);
+    int loc, n_grp;
+    wide_work_item(a.offsets, a.E, ntiles / ntg, x, jb, e, n_grp, loc);
     if (e < 0) return;
+    n_tile = n_grp * ntg;
     row0 = a.offsets[e] + (int64_t)loc * BM;
     m = min(BM, a.offsets[e + 1] - (int)row0);
   }
@@ -302,6 +321,9 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
     const int r = chunk / CH, pc = chunk % CH;
     vb[q] = (uint32_t)(b_row(r) * wrow + 16 * (pc ^ swz<CH>(r)));
   }
+  // the weight rows of n-tile n_tile + t sit t * bstep rows further on (FC1: both the
+  // gate and the up half move by 128 rows)
+  const int64_t bstep = kMode == kModeFC1 ? BN / 2 : BN;
   // Scales move in groups of G stages (32 bytes per row): one 16-byte piece per
   // lane, lane l's piece landing at 16 l, so wave w fills rows [32 w, 32 w + 32) of
   // a [256][32] group buffer with one copy per operand - a quarter of the copy
@@ -310,18 +332,18 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
   // buffer, zeros (range check); those bytes are never used.
   const uint32_t vsa = (uint32_t)(a_src_row(32 * wave + (lane >> 1)) * srow + 16 * (lane & 1));
   const uint32_t vsb = (uint32_t)(b_row(32 * wave + (lane >> 1)) * srow + 16 * (lane & 1));
-  auto issue_scales = [&](WideScales& sc, int grp) {
+  auto issue_scales = [&](WideScales& sc, int grp, int t) {
     buf_dma16(ras, &sc.A[wave * 1024], vsa, (uint32_t)grp * SG);
-    buf_dma16(rbs, &sc.B[wave * 1024], vsb, (uint32_t)grp * SG);
+    buf_dma16(rbs, &sc.B[wave * 1024], vsb, (uint32_t)(grp * SG + t * bstep * srow));
   };
 
-  // copy j (0 .. D-1) of stage st into slot sl: A chunks, then B chunks
-  auto issue_one = [&](WideSlot& sl, int st, int j) {
+  // copy j (0 .. D-1) of stage st of n-tile n_tile + t into slot sl: A chunks, then B chunks
+  auto issue_one = [&](WideSlot& sl, int st, int t, int j) {
     if (j < IA) {
       buf_dma16(ra, &sl.A[(wave * IA + j) * 1024], va[j], (uint32_t)st * R);
     } else {
       const int q = j - IA;
-      buf_dma16(rb, &sl.B[(wave * IB + q) * 1024], vb[q], (uint32_t)st * R);
+      buf_dma16(rb, &sl.B[(wave * IB + q) * 1024], vb[q], (uint32_t)(st * R + t * bstep * wrow));
     }
   };
 
@@ -388,8 +410,8 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
   // stage's scales are stage `sub` of group buffer csc; the last step also copies
   // the next scale group into nsc (when `more_sc`).
   constexpr int DC = (D + S - 1) / S;
-  auto stage = [&](auto kActive, const WideSlot& sl, WideSlot& nsl, bool more, int nst_, const WideScales& csc,
-                   WideScales& nsc, bool more_sc, int grp_next, int sub) {
+  auto stage = [&](auto kActive, const WideSlot& sl, WideSlot& nsl, bool more, int nst_, int t_, const WideScales& csc,
+                   WideScales& nsc, bool more_sc, int grp_next, int t_sc, int sub) {
     constexpr bool act = decltype(kActive)::value;
     int sa[2], sb[4];
     Frags F[2];
@@ -412,9 +434,9 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
       constexpr int s = decltype(S_)::value;
       if (more) {
 #pragma unroll
-        for (int j = s * DC; j < (s + 1) * DC && j < D; ++j) issue_one(nsl, nst_, j);
+        for (int j = s * DC; j < (s + 1) * DC && j < D; ++j) issue_one(nsl, nst_, t_, j);
       }
-      if (s == S - 1 && more_sc) issue_scales(nsc, grp_next);
+      if (s == S - 1 && more_sc) issue_scales(nsc, grp_next, t_sc);
       if constexpr (act) {
         if constexpr (s + 1 < S) load_frags(sl, s + 1, F[(s + 1) & 1]);
         mfma_step(S_, F[s & 1], sa, sb);
@@ -430,9 +452,15 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
 
   // ring of two slots: at stage st wait for its copies (the only ones in flight),
   // barrier (every wave's part has landed and every wave is done with st - 1),
-  // then compute st while the copies of st + 1 go to the other slot
+  // then compute st while the copies of st + 1 go to the other slot. With several
+  // n-tiles per workgroup the ring runs on: the last stage of n-tile t copies stage 0
+  // of n-tile t + 1 (K / 256 is even, so every n-tile starts in slot 0), and its
+  // first scale group goes to buffer 0 in that stage when the n-tile's last group
+  // uses buffer 1, else right after the stage loop.
   const int nst = NST > 0 ? NST : (int)(K / KS);
-  auto run = [&](auto kActive) {
+  const int ngrp = (nst + G - 1) / G;
+  auto run = [&](auto kActive, auto T_) {
+    constexpr int t = decltype(T_)::value;
     auto step = [&](auto I, int st) {
       constexpr int i = decltype(I)::value;
       wait_vmcnt<0>();
@@ -442,7 +470,11 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
       const int grp = st / G;
       WideScales& csc = (grp & 1) ? scl1 : scl0;
       WideScales& nsc = (grp & 1) ? scl0 : scl1;
-      stage(kActive, cur, nxt, st + 1 < nst, st + 1, csc, nsc, st % G == 0 && (grp + 1) * G < nst, grp + 1, st % G);
+      const bool last = st + 1 == nst, next_tile = last && t + 1 < ntg;
+      const bool sc_in_tile = st % G == 0 && grp + 1 < ngrp;
+      const bool sc_next_tile = next_tile && ngrp % 2 == 0;
+      stage(kActive, cur, nxt, !last || next_tile, last ? 0 : st + 1, last ? t + 1 : t, csc, nsc,
+            sc_in_tile || sc_next_tile, sc_in_tile ? grp + 1 : 0, sc_in_tile ? t : t + 1, st % G);
     };
     auto turn = [&](int st0) {
       step(std::integral_constant<int, 0>{}, st0);
@@ -456,13 +488,25 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
     }
   };
 #pragma unroll
-  for (int j = 0; j < D; ++j) issue_one(slot0, 0, j);
-  issue_scales(scl0, 0);
-  if (64 * wm < __builtin_amdgcn_readfirstlane(m)) run(std::true_type{});
-  else run(std::false_type{});
-  if (kMode != kModeFC1) lds_barrier();  // every wave is done reading the ring: its slots become staging
-  wide_epilogue<kMode, kYBF16>(a, acc, reinterpret_cast<uint8_t*>(wave < 4 ? &slot0 : &slot1) + (wave & 3) * STG,
-                               n_tile, row0, m);
+  for (int j = 0; j < D; ++j) issue_one(slot0, 0, 0, j);
+  issue_scales(scl0, 0, 0);
+  const bool active = 64 * wm < __builtin_amdgcn_readfirstlane(m);
+  static_for<0, NTG>([&](auto T_) {
+    constexpr int t = decltype(T_)::value;
+    if (t > 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    }
+    if (active) run(std::true_type{}, T_);
+    else run(std::false_type{}, T_);
+    constexpr bool more_tiles = t + 1 < NTG;
+    if (kMode != kModeFC1 || (more_tiles && ngrp % 2 == 1)) lds_barrier();  // every wave is done with the ring
+    if (more_tiles && ngrp % 2 == 1) issue_scales(scl0, 0, t + 1);
+    // staging (FC2 / dense) in slot 1 only: slot 0 may be receiving the next n-tile's stage 0
+    wide_epilogue<kMode, kYBF16>(a, acc, reinterpret_cast<uint8_t*>(&slot1) + wave * STG, n_tile + t, row0, m);
+  });
 }
 
 template <int kMode, bool kYBF16>
@@ -470,12 +514,40 @@ static void launch_wide_t(const GemmArgs& a, int64_t m_units, hipStream_t stream
   const dim3 grid((unsigned)(8 * cdiv(a.ntiles, 8) * m_units));
   // fully unrolled instances for K = 7168 and K = 2048 (the layer's H and I)
   const int64_t nst = a.K / wide::KS;
-  if (nst == 28) gemm_wide_kernel<kMode, kYBF16, 28><<<grid, 512, 0, stream>>>(a);
-  else if (nst == 8) gemm_wide_kernel<kMode, kYBF16, 8><<<grid, 512, 0, stream>>>(a);
-  else gemm_wide_kernel<kMode, kYBF16, 0><<<grid, 512, 0, stream>>>(a);
+  if constexpr (kMode != kModeDense) {
+    if (nst == 8 && a.ngroup == 4) {
+      gemm_wide_kernel<kMode, kYBF16, 8, 4><<<grid, 512, 0, stream>>>(a);
+      return;
+    }
+    if (nst == 8 && a.ngroup == 2) {
+      gemm_wide_kernel<kMode, kYBF16, 8, 2><<<grid, 512, 0, stream>>>(a);
+      return;
+    }
+  }
+  if (nst == 28) gemm_wide_kernel<kMode, kYBF16, 28, 1><<<grid, 512, 0, stream>>>(a);
+  else if (nst == 8) gemm_wide_kernel<kMode, kYBF16, 8, 1><<<grid, 512, 0, stream>>>(a);
+  else gemm_wide_kernel<kMode, kYBF16, 0, 1><<<grid, 512, 0, stream>>>(a);
 }
 
-void launch_wide_gemm(int mode, bool y_bf16, const GemmArgs& a, int64_t m_units, hipStream_t stream) {
+// Measured on the 16384-token FP4 layer: four n-tiles per workgroup take FC2 (8
+// stages per n-tile) from 1.41 to 1.30 ms; FC1 (28 stages) gains nothing from two,
+// whose unrolled code is twice the size, so it keeps one.
+#ifndef MXF_WIDE_NG_FC2
+#define MXF_WIDE_NG_FC2 4
+#endif
+
+void launch_wide_gemm(int mode, bool y_bf16, const GemmArgs& a_in, int64_t m_units, hipStream_t stream) {
+  // consecutive n-tiles per workgroup for the grouped GEMMs: the ring runs on from
+  // one n-tile into the next, which needs an even stage count
+  GemmArgs a = a_in;
+  a.ngroup = 1;
+  if (MXF_WIDE_ORDER && mode == kModeFC2 && a.K / wide::KS == 8) {
+    for (int ng = MXF_WIDE_NG_FC2; ng > 1; ng /= 2)
+      if (a.ntiles % ng == 0 && (ng == 4 || ng == 2)) {
+        a.ngroup = ng;
+        break;
+      }
+  }
   if (mode == kModeFC1) launch_wide_t<kModeFC1, false>(a, m_units, stream);
   else if (mode == kModeDense) launch_wide_t<kModeDense, false>(a, m_units, stream);
   else if (y_bf16) launch_wide_t<kModeFC2, true>(a, m_units, stream);

@@ -64,6 +64,7 @@ def _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt, rows=None, tokens=None):
     (333, 1024, 1024, 32, 4, "e2m1", 3),   # FP4 x FP4 tiles, some experts empty
     (65, 512, 512, 4, 2, "e4m3", 4),       # just past the streaming threshold
     (700, 2048, 512, 4, 2, "e2m1", 5),     # FP4 x FP4, ~350 rows per expert: full and partial 256-row units
+    (300, 1024, 2048, 8, 2, "e2m1", 6),    # FP4 FC2 with K = 2048: four n-tiles per workgroup
 ])
 def test_layer_small_shapes_full_oracle(T, H, I, E, k, fmt, seed):
     x = dg.activations(seed, T, H)
