@@ -26,7 +26,10 @@ __device__ __forceinline__ void load8(const void* y, int64_t off, float (&v)[8])
   }
 }
 
-template <bool kYBF16, bool kOutBF16>
+// KT > 0: topk is a compile-time constant and the KT gathered rows of a thread are
+// all in flight at once (indices and gates first, then the rows, then the sum in
+// slot order); KT == 0: any topk, one row at a time.
+template <bool kYBF16, bool kOutBF16, int KT>
 __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ y,
                                                       const float* __restrict__ gates,
                                                       const int32_t* __restrict__ pair_row,
@@ -40,13 +43,29 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ y
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  for (int j = 0; j < topk; ++j) {
-    const float g = gates[t * topk + j];
-    const int64_t r = pair_row[t * topk + j];
-    float v[8];
-    load8<kYBF16>(y, r * H + col, v);
+  if constexpr (KT > 0) {
+    int64_t r[KT];
+    float gv[KT], v[KT][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    for (int j = 0; j < KT; ++j) {
+      r[j] = pair_row[t * KT + j];
+      gv[j] = gates[t * KT + j];
+    }
+#pragma unroll
+    for (int j = 0; j < KT; ++j) load8<kYBF16>(y, r[j] * H + col, v[j]);
+#pragma unroll
+    for (int j = 0; j < KT; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(gv[j], v[j][i], acc[i]);
+  } else {
+    for (int j = 0; j < topk; ++j) {
+      const float g = gates[t * topk + j];
+      const int64_t r = pair_row[t * topk + j];
+      float v[8];
+      load8<kYBF16>(y, r * H + col, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    }
   }
   if (kOutBF16) {
     uint32_t w[4];
@@ -66,11 +85,13 @@ int launch_combine(const void* y, bool y_bf16, const float* gates, const int32_t
   if (n == 0) return 0;
   dim3 grid((unsigned)cdiv(n, 256)), block(256);
   if (y_bf16) {
-    if (out_bf16) combine_kernel<true, true><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
-    else combine_kernel<true, false><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
+    if (out_bf16 && topk == 6) combine_kernel<true, true, 6><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
+    else if (out_bf16) combine_kernel<true, true, 0><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
+    else if (topk == 6) combine_kernel<true, false, 6><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
+    else combine_kernel<true, false, 0><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
   } else {
-    if (out_bf16) combine_kernel<false, true><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
-    else combine_kernel<false, false><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
+    if (out_bf16) combine_kernel<false, true, 0><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
+    else combine_kernel<false, false, 0><<<grid, block, 0, stream>>>(y, gates, pair_row, T, topk, H, out);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
