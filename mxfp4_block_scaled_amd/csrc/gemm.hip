@@ -31,7 +31,7 @@ int launch_dense_gemm(const uint8_t* qa, const uint8_t* qa_scale, bool act_fp4, 
     a.M = M;
     a.act_rows = M;
     a.ntiles = (int)(N / tile::BN);
-    launch_tile_gemm(kModeDense, false, act_fp4, a, M, 0, stream);
+    if (launch_tile_gemm(kModeDense, false, act_fp4, a, M, 0, stream)) return -1;
   } else if (dense_ksplit(M, N, K) > 1) {
     const int S = dense_ksplit(M, N, K);
     a.act = qa;
@@ -93,8 +93,8 @@ int launch_grouped_gemm(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, 
     // R rows over at most `slots` non-empty experts, each of which adds at most one partial unit
     f1.ntiles = (int)(I / (tile::BN / 2));
     f2.ntiles = (int)(H / tile::BN);
-    launch_tile_gemm(kModeFC1, false, act_fp4, f1, R, slots, stream);
-    launch_tile_gemm(kModeFC2, y_bf16, act_fp4, f2, R, slots, stream);
+    if (launch_tile_gemm(kModeFC1, false, act_fp4, f1, R, slots, stream)) return -1;
+    if (launch_tile_gemm(kModeFC2, y_bf16, act_fp4, f2, R, slots, stream)) return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -232,8 +232,9 @@ void launch_reduce_partials(const float* part, int S, int64_t n, float* c, hipSt
 void launch_stream_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int mt, dim3 grid,
                         hipStream_t stream);
 // rows: activation rows in all; groups: experts that may hold a partial unit (0 for dense)
-void launch_tile_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int64_t rows, int64_t groups,
-                      hipStream_t stream);
+// returns -1 (nothing launched) when an operand exceeds the tiled kernels' 32-bit offsets
+int launch_tile_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int64_t rows, int64_t groups,
+                     hipStream_t stream);
 void launch_wide_gemm(int mode, bool y_bf16, const GemmArgs& a, int64_t m_units, hipStream_t stream);
 
 }  // namespace mxf

@@ -24,6 +24,9 @@ int launch_combine(const void* y, bool y_bf16, const float* gates, const int32_t
 // number of K slices the dense GEMM splits into (1: none); with more than one it
 // needs dense_ksplit * M * N fp32 of partial sums
 int dense_ksplit(int64_t M, int64_t N, int64_t K);
+// the tiled kernels (many rows per weight matrix) address an activation matrix of
+// `rows` rows and one [N][K/2] weight matrix with 32-bit byte offsets
+bool tile_offsets_fit(int64_t rows, int64_t K, int64_t N, bool act_fp4);
 
 // dense C[M][N] (fp32) = A_hat (already quantised, [M][K] codes + scales) x W_hat^T;
 // partials: dense_ksplit(M, N, K) * M * N fp32 of scratch when that is above 1

@@ -77,6 +77,9 @@ def test_gemm_errors():
     assert lib.mxfp4_gemm(A, 16, 32, 4096, 0, A, A, A, None, need, None) == WORKSPACE
     assert lib.mxfp4_gemm(A, 16, 32, 4096, 0, A, U, A, A, need, None) == ALIGN
     assert lib.mxfp4_gemm(None, 0, 32, 4096, 0, None, None, None, None, 0, None) == OK
+    # M > 64 with N % 256 == 0 runs the tiled kernels: operands below 4 GiB (32-bit offsets)
+    assert lib.mxfp4_gemm(A, 1 << 20, 256, 8192, 0, A, A, A, A, 1 << 40, None) == UNSUPPORTED
+    assert lib.mxfp4_gemm(A, 1 << 20, 272, 8192, 0, A, A, A, A, need, None) == WORKSPACE  # streamed path: no limit
 
 
 def test_route_errors():
@@ -111,6 +114,11 @@ def test_grouped_gemm_errors():
     assert call(w2=None) == NULL
     assert call(h=U) == ALIGN
     assert call(E=4096) == UNSUPPORTED
+    # tiled path (T > 64): q, h and one expert's weights must stay below 4 GiB (32-bit offsets)
+    assert call(T=600_000) == UNSUPPORTED            # q = 600000 x 7168 bytes (E4M3)
+    assert call(T=1_000_000, fmt=1) == UNSUPPORTED   # h = 6e6 x 1024 bytes (E2M1)
+    assert call(T=600_000, fmt=1, k=1, w2=None) == NULL  # fits: checked up to the NULL test, nothing runs
+    assert call(H=1 << 20, I=4096, T=100) == UNSUPPORTED  # w1 = 8192 x 2^19 bytes per expert
     assert call(T=0, q=None) == OK
 
 
