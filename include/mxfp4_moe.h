@@ -99,7 +99,8 @@ int mxfp4_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t K, int 
  * Requires K % 512 == 0 (one 512-k super-step of scaled-MFMA K steps) and
  * N % 16 == 0; M >= 0 (M == 0 is a no-op). For M > 64 with N % 256 == 0 (the
  * tiled kernels) the quantised activations and the weight codes must each stay
- * below 4 GiB, else UNSUPPORTED.
+ * below 4 GiB, else UNSUPPORTED; otherwise (the weight-streaming kernel) 64
+ * weight rows must stay below 4 GiB (K < 2^27), else UNSUPPORTED.
  * Errors: NULL, SHAPE, ALIGN, FORMAT, WORKSPACE, UNSUPPORTED.
  */
 size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_fmt);
@@ -141,8 +142,8 @@ int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t topk,
  * Row r of the permuted order is token sorted_pair[r] / topk. The grid is sized
  * from T and topk; per-expert counts are read on the device.
  * Requires H % 512 == 0, I % 512 == 0, 1 <= topk <= min(E, 8), E <= 1024;
- * for T > 64 (the tiled kernels) q, h and one expert's w1 and w2 codes must each
- * stay below 4 GiB, else UNSUPPORTED. T == 0 is a no-op.
+ * one expert's w1 and w2 codes must each stay below 4 GiB, and for T > 64 (the
+ * tiled kernels) so must q and h, else UNSUPPORTED. T == 0 is a no-op.
  * Errors: NULL, SHAPE, ALIGN, FORMAT, UNSUPPORTED.
  */
 int moe_grouped_mxfp4_gemm(const uint8_t* q, const uint8_t* q_scale, int act_fmt,

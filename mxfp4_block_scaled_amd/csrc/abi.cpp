@@ -64,6 +64,8 @@ int mxfp4_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K, int act_fmt, 
   if (!valid_elem(act_fmt)) return MXF_ERR_FORMAT;
   if (M < 0 || M > kMaxRows || N <= 0 || N % 16 != 0 || K <= 0 || K % 512 != 0) return MXF_ERR_SHAPE;
   if (M > 64 && N % 256 == 0 && !mxf::tile_offsets_fit(M, K, N, act_fmt == MXF_E2M1)) return MXF_ERR_UNSUPPORTED;
+  // the streaming kernel addresses 64 weight rows of a workgroup with 32-bit offsets
+  if ((M <= 64 || N % 256 != 0) && 64 * (K / 2) >= ((int64_t)1 << 32)) return MXF_ERR_UNSUPPORTED;
   if (M == 0) return MXF_OK;
   if (!a || !w || !w_scale || !c) return MXF_ERR_NULL;
   if (!aligned16(a) || !aligned16(w) || !aligned16(w_scale) || !aligned16(c)) return MXF_ERR_ALIGN;
@@ -105,6 +107,8 @@ int moe_grouped_mxfp4_gemm(const uint8_t* q, const uint8_t* q_scale, int act_fmt
   if (T < 0 || topk < 1 || topk > 8 || E < 1 || topk > E) return MXF_ERR_SHAPE;
   if (H <= 0 || H % 512 != 0 || I <= 0 || I % 512 != 0) return MXF_ERR_SHAPE;
   if (E > 1024 || T * (int64_t)topk > kMaxRows) return MXF_ERR_UNSUPPORTED;
+  // one expert's w1 and w2 codes are addressed with 32-bit offsets by every kernel
+  if (2 * I * (H / 2) >= ((int64_t)1 << 32) || H * (I / 2) >= ((int64_t)1 << 32)) return MXF_ERR_UNSUPPORTED;
   if (T > 64 && (!mxf::tile_offsets_fit(T, H, 2 * I, act_fmt == MXF_E2M1) ||
                  !mxf::tile_offsets_fit(T * topk, I, H, act_fmt == MXF_E2M1)))
     return MXF_ERR_UNSUPPORTED;

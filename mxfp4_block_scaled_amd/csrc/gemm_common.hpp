@@ -212,6 +212,14 @@ __device__ __forceinline__ v4i buf_load16(buf_rsrc r, uint32_t voff, uint32_t so
   return v4i{};
 #endif
 }
+// non-temporal form (cache policy NT: lines read once, not kept in the caches)
+__device__ __forceinline__ v4i buf_load16_nt(buf_rsrc r, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2);
+#else
+  return v4i{};
+#endif
+}
 __device__ __forceinline__ int buf_load4(buf_rsrc r, uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);

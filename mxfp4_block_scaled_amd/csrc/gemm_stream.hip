@@ -1,8 +1,9 @@
 // Weight-streaming MXFP4 GEMM for few rows per expert (decode, small dense M):
-// weights go straight from HBM to registers in the 16x16x128 scaled MFMA's lane
-// layout, the K range is split over the 4 waves of a workgroup and reduced
-// through LDS in a fixed order. One workgroup = one expert x 64 weight rows
-// (FC1: 32 gate + the 32 matching up rows, so SwiGLU stays local).
+// every weight byte is read once, as whole 128-byte lines with non-temporal
+// loads, and turned into the 16x16x128 scaled MFMA's lane layout through a small
+// per-wave LDS area; the K range is split over the 4 waves of a workgroup and
+// reduced through LDS in a fixed order. One workgroup = one expert x 64 weight
+// rows (FC1: 32 gate + the 32 matching up rows, so SwiGLU stays local).
 #include "gemm_common.hpp"
 
 namespace mxf {
@@ -53,9 +54,9 @@ __device__ __forceinline__ void epilogue_fc1(const float (&tot)[4][4], int local
 // weight-streaming kernel (rows per expert <= 16 * MT)
 //
 // K order inside a 512-k super-step: step s, hardware block hb <-> memory block
-// 4 s + hb. Then the 4 lane groups of a row read 64 contiguous bytes per load
-// instruction (16 bytes each, FP4), and an FP8 lane's two 16-byte halves sit at
-// 128 s + 16 g and 128 s + 64 + 16 g. The scale of (row, block 4 s + g) is byte
+// 4 s + hb. An FP4 activation lane (g, r16) then reads its 16 bytes of step s at
+// 64 s + 16 g, and an FP8 lane's two 16-byte halves sit at 128 s + 16 g and
+// 128 s + 64 + 16 g. The scale of (row, block 4 s + g) is byte
 // 4 s + g of the row's 16 scale bytes, so a lane gathers bytes g, 4+g, 8+g and
 // 12+g of them into one register (op_sel = s picks byte s).
 __device__ __forceinline__ int gather_scales(v4i d, int g) {
@@ -64,10 +65,23 @@ __device__ __forceinline__ int gather_scales(v4i d, int g) {
                ((((uint32_t)d[2] >> sh) & 0xFFu) << 16) | ((((uint32_t)d[3] >> sh) & 0xFFu) << 24));
 }
 
+// Weight loads read whole 128-byte lines with non-temporal loads (lines read once
+// per launch): load instruction s of a 16-row fragment gives lane 8 q + j row
+// 8 (s & 1) + q of the fragment and 16-byte block 8 (s >> 1) + ((j + q) & 7) of
+// that row's 256-byte super-step chunk. Each wave then moves a fragment through a
+// private LDS area into the MFMA lane layout (lane (g, r16): row r16, block
+// 4 s + g). Instruction s is stored at s * kStgStride + 16 lane; the stride is
+// 128 (mod 256) bytes off for odd s and the rotation by q spreads the 16 rows
+// read by a lane group over all 64 banks.
+constexpr int kStgStride = 1152;
+constexpr int kStgBytes = 4 * kStgStride;
+
 template <bool kActFP4, int kMode, bool kYBF16, int MT>
-__global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
+__device__ __forceinline__ void stream_body(const GemmArgs& a) {
   constexpr int kFA = kActFP4 ? kFmtFP4 : kFmtFP8;
-  __shared__ float red[4][MT * 16][64];
+  // per wave: two fragment staging areas in the loop, then MT x 16 x 64 fp32 partial sums
+  constexpr int kWaveBytes = 2 * kStgBytes > MT * 4096 ? 2 * kStgBytes : MT * 4096;
+  __shared__ v4i lds[4][kWaveBytes / 16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
 
   int e = 0;
@@ -86,25 +100,40 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
   const int64_t wrow_bytes = K / 2, srow_bytes = K / 32;
   const int64_t arow_bytes = kActFP4 ? K / 2 : K;
 
-  // the 4 weight fragments of this workgroup
-  const uint8_t* wp[4];
-  const uint8_t* sp[4];
+  // the 4 weight fragments of this workgroup: rows n0 + roff[f] + [0, 16), read through
+  // buffer resources over the workgroup's row span (below 4 GiB, checked on the host)
+  int64_t n0, span;
+  int roff[4];
   bool fvalid[4];
+  if (kMode == kModeFC1) {
+    n0 = (int64_t)blockIdx.x * 32;  // gate rows n0 + [0, 32), up rows I + n0 + [0, 32)
+    span = a.I + 32;
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    int64_t n;
-    if (kMode == kModeFC1) {
-      const int64_t i0 = (int64_t)blockIdx.x * 32 + 16 * (f & 1);
-      n = (f < 2 ? 0 : a.I) + i0;
+    for (int f = 0; f < 4; ++f) {
+      roff[f] = (f < 2 ? 0 : (int)a.I) + 16 * (f & 1);
       fvalid[f] = true;
-    } else {
-      n = (int64_t)blockIdx.x * 64 + 16 * f;
-      fvalid[f] = n < a.N;
     }
-    const int64_t nr = n + r16;
-    wp[f] = a.w + ((int64_t)e * a.N + nr) * wrow_bytes + 16 * g;
-    sp[f] = a.w_scale + ((int64_t)e * a.N + nr) * srow_bytes;
+  } else {
+    n0 = (int64_t)blockIdx.x * 64;
+    span = min((int64_t)64, a.N - n0);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      roff[f] = 16 * f;
+      fvalid[f] = 16 * f < span;
+    }
   }
+  const int64_t rbase = (int64_t)e * a.N + n0;
+  const buf_rsrc wr = make_rsrc(a.w + rbase * wrow_bytes, (uint32_t)(span * wrow_bytes));
+  const buf_rsrc sr = make_rsrc(a.w_scale + rbase * srow_bytes, (uint32_t)(span * srow_bytes));
+  const int q = lane >> 3, rot = ((lane & 7) + q) & 7;
+  const uint32_t wvoff = (uint32_t)(q * wrow_bytes + 16 * rot);
+  const uint32_t svoff = (uint32_t)(r16 * srow_bytes);
+  // LDS byte offsets: where this lane's loaded block goes, and where its MFMA operand of step s is
+  uint8_t* const stg = reinterpret_cast<uint8_t*>(&lds[wave][0]);
+  int rd[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    rd[s] = (2 * (s >> 1) + (r16 >> 3)) * kStgStride + 128 * (r16 & 7) + 16 * ((4 * s + g - (r16 & 7)) & 7);
   // activation rows of the MT fragments
   const uint8_t* ap[MT];
   const uint8_t* asp[MT];
@@ -139,57 +168,75 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
   const int len = ss_hi - ss_lo;
   const int ss_begin = ss_lo + wave * len / 4, ss_end = ss_lo + (wave + 1) * len / 4;
   for (int ss = ss_begin; ss < ss_end; ++ss) {
-    v4i bq[4][4];
-    int bs[4];
+    // issue every load of the super-step before any wait: activations and scales
+    // (few bytes, mostly L2 hits; rows past m read row 0 and are zeroed below),
+    // then the 16 weight lines
+    v4i araw[MT][kActFP4 ? 4 : 8], asraw[MT], sraw[4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (kActFP4) {
+        const uint8_t* src = ap[mt] + (int64_t)ss * 256;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) araw[mt][s] = *reinterpret_cast<const v4i*>(src + 64 * s);
+      } else {
+        const uint8_t* base = ap[mt] + (int64_t)ss * 512;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          araw[mt][2 * s] = *reinterpret_cast<const v4i*>(base + 128 * s);
+          araw[mt][2 * s + 1] = *reinterpret_cast<const v4i*>(base + 128 * s + 64);
+        }
+      }
+      asraw[mt] = *reinterpret_cast<const v4i*>(asp[mt] + (int64_t)ss * 16);
+    }
+    v4i raw[4][4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       if (fvalid[f]) {
-        const uint8_t* src = wp[f] + (int64_t)ss * 256;
+        sraw[f] = buf_load16(sr, svoff, (uint32_t)(roff[f] * srow_bytes + ss * 16));
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bq[f][s] = *reinterpret_cast<const v4i*>(src + 64 * s);
-        bs[f] = gather_scales(*reinterpret_cast<const v4i*>(sp[f] + (int64_t)ss * 16), g);
+        for (int s = 0; s < 4; ++s)
+          raw[f][s] = buf_load16_nt(wr, wvoff + 128 * (s >> 1),
+                                    (uint32_t)((roff[f] + 8 * (s & 1)) * wrow_bytes + ss * 256));
       } else {
+        sraw[f] = v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bq[f][s] = v4i{0, 0, 0, 0};
-        bs[f] = 0;
+        for (int s = 0; s < 4; ++s) raw[f][s] = v4i{0, 0, 0, 0};
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    v8i aq[MT][4];
+    int as[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      v8i aq[4];
-      int as = 0;
-      if (avalid[mt]) {
-        if (kActFP4) {
-          const uint8_t* src = ap[mt] + (int64_t)ss * 256;
+      const v4i z = v4i{0, 0, 0, 0};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            v4i x = *reinterpret_cast<const v4i*>(src + 64 * s);
-            aq[s] = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
-          }
-        } else {
-          const uint8_t* base = ap[mt] + (int64_t)ss * 512;
+      for (int s = 0; s < 4; ++s) {
+        const v4i lo = avalid[mt] ? araw[mt][kActFP4 ? s : 2 * s] : z;
+        const v4i hi = kActFP4 || !avalid[mt] ? z : araw[mt][kActFP4 ? s : 2 * s + 1];
+        aq[mt][s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      as[mt] = avalid[mt] ? gather_scales(asraw[mt], g) : 0;
+    }
+    int bs[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            v4i lo = *reinterpret_cast<const v4i*>(base + 128 * s);
-            v4i hi = *reinterpret_cast<const v4i*>(base + 128 * s + 64);
-            aq[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-        }
-        as = gather_scales(*reinterpret_cast<const v4i*>(asp[mt] + (int64_t)ss * 16), g);
-      } else {
+    for (int f = 0; f < 4; ++f) bs[f] = gather_scales(sraw[f], g);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) aq[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int f = 0; f < 4; ++f) {
+      uint8_t* const area = stg + (f & 1) * kStgBytes;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) *reinterpret_cast<v4i*>(area + s * kStgStride + 16 * lane) = raw[f][s];
+      v8i b[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const v4i x = *reinterpret_cast<const v4i*>(area + rd[s]);
+        b[s] = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
       }
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        v8i b0 = v8i{bq[f][0][0], bq[f][0][1], bq[f][0][2], bq[f][0][3], 0, 0, 0, 0};
-        v8i b1 = v8i{bq[f][1][0], bq[f][1][1], bq[f][1][2], bq[f][1][3], 0, 0, 0, 0};
-        v8i b2 = v8i{bq[f][2][0], bq[f][2][1], bq[f][2][2], bq[f][2][3], 0, 0, 0, 0};
-        v8i b3 = v8i{bq[f][3][0], bq[f][3][1], bq[f][3][2], bq[f][3][3], 0, 0, 0, 0};
-        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 0>(aq[0], b0, acc[mt][f], as, bs[f]);
-        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 1>(aq[1], b1, acc[mt][f], as, bs[f]);
-        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 2>(aq[2], b2, acc[mt][f], as, bs[f]);
-        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 3>(aq[3], b3, acc[mt][f], as, bs[f]);
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 0>(aq[mt][0], b[0], acc[mt][f], as[mt], bs[f]);
+        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 1>(aq[mt][1], b[1], acc[mt][f], as[mt], bs[f]);
+        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 2>(aq[mt][2], b[2], acc[mt][f], as[mt], bs[f]);
+        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 3>(aq[mt][3], b[3], acc[mt][f], as[mt], bs[f]);
       }
     }
   }
@@ -198,12 +245,14 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
                         ? static_cast<void*>(static_cast<float*>(a.out) + (int64_t)blockIdx.y * a.M * a.N)
                         : a.out;
   // reduce the 4 K-slices in a fixed order (deterministic)
+  // (each wave writes only its own area, which it alone used in the loop)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][mt * 16 + f * 4 + v][lane] = acc[mt][f][v];
+      for (int v = 0; v < 4; ++v)
+        reinterpret_cast<float*>(&lds[wave][0])[(mt * 16 + f * 4 + v) * 64 + lane] = acc[mt][f][v];
   __syncthreads();
   for (int mt = wave; mt < MT; mt += 4) {
     float tot[4][4];
@@ -212,7 +261,9 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int idx = mt * 16 + f * 4 + v;
-        tot[f][v] = ((red[0][idx][lane] + red[1][idx][lane]) + red[2][idx][lane]) + red[3][idx][lane];
+        const float* r = reinterpret_cast<const float*>(&lds[0][0]) + idx * 64 + lane;
+        constexpr int kW = kWaveBytes / 4;  // floats per wave area
+        tot[f][v] = ((r[0] + r[kW]) + r[2 * kW]) + r[3 * kW];
       }
     if (kMode == kModeFC1) {
       epilogue_fc1<kActFP4>(tot, 16 * mt, m, row0, (int64_t)blockIdx.x * 32, a.I, a.h, a.h_scale);
@@ -232,10 +283,22 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
   }
 }
 
+// One 16-row fragment (decode): registers held to three waves per SIMD (168
+// VGPRs), with the 16 weight lines of a super-step in flight per wave; measured
+// faster than two waves per SIMD with the same loads or three waves with fewer.
+template <bool kActFP4, int kMode, bool kYBF16>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) gemm_stream1_kernel(GemmArgs a) {
+  stream_body<kActFP4, kMode, kYBF16, 1>(a);
+}
+template <bool kActFP4, int kMode, bool kYBF16, int MT>
+__global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
+  stream_body<kActFP4, kMode, kYBF16, MT>(a);
+}
+
 template <bool kActFP4, int kMode, bool kYBF16>
 static void launch_stream_mt(const GemmArgs& a, int mt, dim3 grid, hipStream_t stream) {
   switch (mt) {
-    case 1: gemm_stream_kernel<kActFP4, kMode, kYBF16, 1><<<grid, 256, 0, stream>>>(a); break;
+    case 1: gemm_stream1_kernel<kActFP4, kMode, kYBF16><<<grid, 256, 0, stream>>>(a); break;
     case 2: gemm_stream_kernel<kActFP4, kMode, kYBF16, 2><<<grid, 256, 0, stream>>>(a); break;
     case 3: gemm_stream_kernel<kActFP4, kMode, kYBF16, 3><<<grid, 256, 0, stream>>>(a); break;
     default: gemm_stream_kernel<kActFP4, kMode, kYBF16, 4><<<grid, 256, 0, stream>>>(a); break;

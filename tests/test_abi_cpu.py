@@ -79,7 +79,10 @@ def test_gemm_errors():
     assert lib.mxfp4_gemm(None, 0, 32, 4096, 0, None, None, None, None, 0, None) == OK
     # M > 64 with N % 256 == 0 runs the tiled kernels: operands below 4 GiB (32-bit offsets)
     assert lib.mxfp4_gemm(A, 1 << 20, 256, 8192, 0, A, A, A, A, 1 << 40, None) == UNSUPPORTED
-    assert lib.mxfp4_gemm(A, 1 << 20, 272, 8192, 0, A, A, A, A, need, None) == WORKSPACE  # streamed path: no limit
+    assert lib.mxfp4_gemm(A, 1 << 20, 272, 8192, 0, A, A, A, A, need, None) == WORKSPACE  # streamed path
+    # the streamed path addresses 64 weight rows (64 x K/2 bytes) with 32-bit offsets
+    assert lib.mxfp4_gemm(A, 16, 32, 1 << 27, 0, A, A, A, A, 1 << 40, None) == UNSUPPORTED
+    assert lib.mxfp4_gemm(A, 16, 32, (1 << 27) - 512, 0, A, A, A, A, 0, None) == WORKSPACE
 
 
 def test_route_errors():
@@ -119,6 +122,8 @@ def test_grouped_gemm_errors():
     assert call(T=1_000_000, fmt=1) == UNSUPPORTED   # h = 6e6 x 1024 bytes (E2M1)
     assert call(T=600_000, fmt=1, k=1, w2=None) == NULL  # fits: checked up to the NULL test, nothing runs
     assert call(H=1 << 20, I=4096, T=100) == UNSUPPORTED  # w1 = 8192 x 2^19 bytes per expert
+    assert call(H=1 << 20, I=4096, T=8) == UNSUPPORTED    # the streaming kernel too
+    assert call(H=1 << 20, I=2048, T=8, w2=None) == NULL  # 4096 x 2^19 bytes: fits
     assert call(T=0, q=None) == OK
 
 
