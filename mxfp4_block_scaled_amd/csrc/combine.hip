@@ -8,21 +8,29 @@
 
 namespace mxf {
 
+// y is read exactly once and out written once, each as whole lines (a wave covers
+// 1 KB of one row): both go through non-temporal loads / stores, which measured
+// faster for this single pass than cached accesses.
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
 template <bool kYBF16>
 __device__ __forceinline__ void load8(const void* y, int64_t off, float (&v)[8]) {
   if (kYBF16) {
-    uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + off);
-    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    const u4v w = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(static_cast<const uint16_t*>(y) + off));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[2 * j] = __uint_as_float(ws[j] << 16);
-      v[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(y) + off);
-    float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const f4v* p = reinterpret_cast<const f4v*>(static_cast<const float*>(y) + off);
+    const f4v a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = a[j];
+      v[4 + j] = b[j];
+    }
   }
 }
 
@@ -68,14 +76,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ y
     }
   }
   if (kOutBF16) {
-    uint32_t w[4];
+    u4v w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = bf16_round(acc[2 * i]) | (bf16_round(acc[2 * i + 1]) << 16);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + t * H + col) = make_uint4(w[0], w[1], w[2], w[3]);
+    __builtin_nontemporal_store(w, reinterpret_cast<u4v*>(static_cast<uint16_t*>(out) + t * H + col));
   } else {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + t * H + col);
-    p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    f4v* p = reinterpret_cast<f4v*>(static_cast<float*>(out) + t * H + col);
+    __builtin_nontemporal_store(f4v{acc[0], acc[1], acc[2], acc[3]}, p);
+    __builtin_nontemporal_store(f4v{acc[4], acc[5], acc[6], acc[7]}, p + 1);
   }
 }
 

@@ -194,9 +194,9 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&ac
           const int idx = lane + 64 * j;
           const int rr = idx >> 4, c8 = idx & 15;
           const int lrow = 64 * wm + 32 * fm + 16 * hh + rr;
-          if (lrow < m)
-            *reinterpret_cast<uint4*>(out + (row0 + lrow) * a.N + col0 + 8 * c8) =
-                *reinterpret_cast<const uint4*>(&ob[rr][8 * c8]);
+          if (lrow < m)  // y is read once, by the combine: non-temporal stores
+            __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(&ob[rr][8 * c8]),
+                                        reinterpret_cast<v4i*>(out + (row0 + lrow) * a.N + col0 + 8 * c8));
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
@@ -221,8 +221,8 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&ac
           const int rr = idx >> 5, c4 = idx & 31;
           const int lrow = 64 * wm + 32 * fm + 8 * hh + rr;
           if (lrow < m)
-            *reinterpret_cast<float4*>(out + (row0 + lrow) * a.N + col0 + 4 * c4) =
-                *reinterpret_cast<const float4*>(&of[rr][4 * c4]);
+            __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(&of[rr][4 * c4]),
+                                        reinterpret_cast<v4i*>(out + (row0 + lrow) * a.N + col0 + 4 * c4));
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
