@@ -76,13 +76,19 @@ __device__ __forceinline__ int gather_scales(v4i d, int g) {
 constexpr int kStgStride = 1152;
 constexpr int kStgBytes = 4 * kStgStride;
 
-template <bool kActFP4, int kMode, bool kYBF16, int MT>
+// NB: consecutive 64-row blocks per workgroup (FC2 / dense only), streamed one after
+// the other by every wave, so that a wave of a short-K GEMM streams NB super-steps
+template <bool kActFP4, int kMode, bool kYBF16, int MT, int NB = 1>
 __device__ __forceinline__ void stream_body(const GemmArgs& a) {
+  static_assert(NB == 1 || kMode != kModeFC1, "FC1 workgroups own one 64-row block");
   constexpr int kFA = kActFP4 ? kFmtFP4 : kFmtFP8;
-  // per wave: two fragment staging areas in the loop, then MT x 16 x 64 fp32 partial sums
-  constexpr int kWaveBytes = 2 * kStgBytes > MT * 4096 ? 2 * kStgBytes : MT * 4096;
+  // per wave: two fragment staging areas in the loop, then NB x MT x 16 x 64 fp32 partial sums
+  constexpr int kWaveBytes = 2 * kStgBytes > NB * MT * 4096 ? 2 * kStgBytes : NB * MT * 4096;
   __shared__ v4i lds[4][kWaveBytes / 16];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  // wave-uniform values made visible as such (readfirstlane), so that the K range, and
+  // with it every buffer load's scalar offset, stays in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
 
   int e = 0;
   int64_t row0 = 0;
@@ -100,29 +106,34 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
   const int64_t wrow_bytes = K / 2, srow_bytes = K / 32;
   const int64_t arow_bytes = kActFP4 ? K / 2 : K;
 
-  // the 4 weight fragments of this workgroup: rows n0 + roff[f] + [0, 16), read through
-  // buffer resources over the workgroup's row span (below 4 GiB, checked on the host)
+  // the 4 weight fragments of each of the NB row blocks: rows n0 + roff[nb][f] + [0, 16),
+  // read through buffer resources over the workgroup's row span (below 4 GiB,
+  // checked on the host)
   int64_t n0, span;
-  int roff[4];
-  bool fvalid[4];
+  int roff[NB][4];
+  bool fvalid[NB][4];
   if (kMode == kModeFC1) {
     n0 = (int64_t)blockIdx.x * 32;  // gate rows n0 + [0, 32), up rows I + n0 + [0, 32)
     span = a.I + 32;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      roff[f] = (f < 2 ? 0 : (int)a.I) + 16 * (f & 1);
-      fvalid[f] = true;
+      roff[0][f] = (f < 2 ? 0 : (int)a.I) + 16 * (f & 1);
+      fvalid[0][f] = true;
     }
   } else {
-    n0 = (int64_t)blockIdx.x * 64;
-    span = min((int64_t)64, a.N - n0);
+    n0 = (int64_t)blockIdx.x * 64 * NB;
+    span = min((int64_t)64 * NB, a.N - n0);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      roff[f] = 16 * f;
-      fvalid[f] = 16 * f < span;
-    }
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        roff[nb][f] = 64 * nb + 16 * f;
+        fvalid[nb][f] = 64 * nb + 16 * f < span;
+      }
   }
-  const int64_t rbase = (int64_t)e * a.N + n0;
+  // the expert index is workgroup-uniform; readfirstlane lets the compiler see that,
+  // so the resources sit in scalar registers (no waterfall loop around each load)
+  const int64_t rbase = (int64_t)__builtin_amdgcn_readfirstlane(e) * a.N + n0;
   const buf_rsrc wr = make_rsrc(a.w + rbase * wrow_bytes, (uint32_t)(span * wrow_bytes));
   const buf_rsrc sr = make_rsrc(a.w_scale + rbase * srow_bytes, (uint32_t)(span * srow_bytes));
   const int q = lane >> 3, rot = ((lane & 7) + q) & 7;
@@ -151,11 +162,13 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
     asp[mt] = a.act_scale + src * srow_bytes;
   }
 
-  v4f acc[MT][4];
+  v4f acc[NB][MT][4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int f = 0; f < 4; ++f) acc[mt][f] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc[nb][mt][f] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // dense with kchunk > 0: grid.y slice s covers super-steps [s kchunk, (s+1) kchunk)
   // and writes its partial sums to slice s of out ([grid.y][M][N])
@@ -188,55 +201,62 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
       }
       asraw[mt] = *reinterpret_cast<const v4i*>(asp[mt] + (int64_t)ss * 16);
     }
-    v4i raw[4][4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      if (fvalid[f]) {
-        sraw[f] = buf_load16(sr, svoff, (uint32_t)(roff[f] * srow_bytes + ss * 16));
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          raw[f][s] = buf_load16_nt(wr, wvoff + 128 * (s >> 1),
-                                    (uint32_t)((roff[f] + 8 * (s & 1)) * wrow_bytes + ss * 256));
-      } else {
-        sraw[f] = v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) raw[f][s] = v4i{0, 0, 0, 0};
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
     v8i aq[MT][4];
     int as[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const v4i z = v4i{0, 0, 0, 0};
+    for (int nb = 0; nb < NB; ++nb) {
+      // the next block's loads go out only after this block's LDS work (a compiler
+      // memory fence on their offsets): one block's 16 lines in flight per wave
+      uint32_t wv = wvoff, sv = svoff;
+      if (nb > 0) asm volatile("" : "+v"(wv), "+v"(sv)::"memory");
+      // a fragment past N (a ragged last block) re-reads the block's first fragment,
+      // so every load stays inside the resource without a branch; its outputs are
+      // never stored
+      v4i raw[4][4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const v4i lo = avalid[mt] ? araw[mt][kActFP4 ? s : 2 * s] : z;
-        const v4i hi = kActFP4 || !avalid[mt] ? z : araw[mt][kActFP4 ? s : 2 * s + 1];
-        aq[mt][s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      for (int f = 0; f < 4; ++f) {
+        const int ro = fvalid[nb][f] ? roff[nb][f] : 0;
+        sraw[f] = buf_load16(sr, sv, (uint32_t)(ro * srow_bytes + ss * 16));
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          raw[f][s] = buf_load16_nt(wr, wv + 128 * (s >> 1), (uint32_t)((ro + 8 * (s & 1)) * wrow_bytes + ss * 256));
       }
-      as[mt] = avalid[mt] ? gather_scales(asraw[mt], g) : 0;
-    }
-    int bs[4];
+      __builtin_amdgcn_sched_barrier(0);
+      if (nb == 0) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) bs[f] = gather_scales(sraw[f], g);
+        for (int mt = 0; mt < MT; ++mt) {
+          const v4i z = v4i{0, 0, 0, 0};
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      uint8_t* const area = stg + (f & 1) * kStgBytes;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) *reinterpret_cast<v4i*>(area + s * kStgStride + 16 * lane) = raw[f][s];
-      v8i b[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const v4i x = *reinterpret_cast<const v4i*>(area + rd[s]);
-        b[s] = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+          for (int s = 0; s < 4; ++s) {
+            const v4i lo = avalid[mt] ? araw[mt][kActFP4 ? s : 2 * s] : z;
+            const v4i hi = kActFP4 || !avalid[mt] ? z : araw[mt][kActFP4 ? s : 2 * s + 1];
+            aq[mt][s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+          as[mt] = avalid[mt] ? gather_scales(asraw[mt], g) : 0;
+        }
       }
+      int bs[4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 0>(aq[mt][0], b[0], acc[mt][f], as[mt], bs[f]);
-        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 1>(aq[mt][1], b[1], acc[mt][f], as[mt], bs[f]);
-        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 2>(aq[mt][2], b[2], acc[mt][f], as[mt], bs[f]);
-        acc[mt][f] = mfma16x16x128<kFA, kFmtFP4, 3>(aq[mt][3], b[3], acc[mt][f], as[mt], bs[f]);
+      for (int f = 0; f < 4; ++f) bs[f] = gather_scales(sraw[f], g);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        uint8_t* const area = stg + (f & 1) * kStgBytes;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) *reinterpret_cast<v4i*>(area + s * kStgStride + 16 * lane) = raw[f][s];
+        v8i b[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const v4i x = *reinterpret_cast<const v4i*>(area + rd[s]);
+          b[s] = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          v4f& c = acc[nb][mt][f];
+          c = mfma16x16x128<kFA, kFmtFP4, 0>(aq[mt][0], b[0], c, as[mt], bs[f]);
+          c = mfma16x16x128<kFA, kFmtFP4, 1>(aq[mt][1], b[1], c, as[mt], bs[f]);
+          c = mfma16x16x128<kFA, kFmtFP4, 2>(aq[mt][2], b[2], c, as[mt], bs[f]);
+          c = mfma16x16x128<kFA, kFmtFP4, 3>(aq[mt][3], b[3], c, as[mt], bs[f]);
+        }
       }
     }
   }
@@ -247,20 +267,24 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
   // reduce the 4 K-slices in a fixed order (deterministic)
   // (each wave writes only its own area, which it alone used in the loop)
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        reinterpret_cast<float*>(&lds[wave][0])[(mt * 16 + f * 4 + v) * 64 + lane] = acc[mt][f][v];
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          reinterpret_cast<float*>(&lds[wave][0])[((nb * MT + mt) * 16 + f * 4 + v) * 64 + lane] = acc[nb][mt][f][v];
   __syncthreads();
-  for (int mt = wave; mt < MT; mt += 4) {
+  // one (row block, 16-row fragment) item per wave
+  for (int item = wave; item < NB * MT; item += 4) {
+    const int nb = item / MT, mt = item % MT;
     float tot[4][4];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int idx = mt * 16 + f * 4 + v;
+        const int idx = item * 16 + f * 4 + v;
         const float* r = reinterpret_cast<const float*>(&lds[0][0]) + idx * 64 + lane;
         constexpr int kW = kWaveBytes / 4;  // floats per wave area
         tot[f][v] = ((r[0] + r[kW]) + r[2 * kW]) + r[3 * kW];
@@ -274,8 +298,8 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
         if (lr < m) {
 #pragma unroll
           for (int f = 0; f < 4; ++f) {
-            const int64_t n = (int64_t)blockIdx.x * 64 + 16 * f + r16;
-            if (fvalid[f]) store_out<kYBF16>(out, (row0 + lr) * a.N + n, tot[f][v]);
+            const int64_t n = n0 + 64 * nb + 16 * f + r16;
+            if (64 * nb + 16 * f < span) store_out<kYBF16>(out, (row0 + lr) * a.N + n, tot[f][v]);
           }
         }
       }
@@ -286,19 +310,31 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
 // One 16-row fragment (decode): registers held to three waves per SIMD (168
 // VGPRs), with the 16 weight lines of a super-step in flight per wave; measured
 // faster than two waves per SIMD with the same loads or three waves with fewer.
-template <bool kActFP4, int kMode, bool kYBF16>
+template <bool kActFP4, int kMode, bool kYBF16, int NB>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) gemm_stream1_kernel(GemmArgs a) {
-  stream_body<kActFP4, kMode, kYBF16, 1>(a);
+  stream_body<kActFP4, kMode, kYBF16, 1, NB>(a);
 }
 template <bool kActFP4, int kMode, bool kYBF16, int MT>
 __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
   stream_body<kActFP4, kMode, kYBF16, MT>(a);
 }
 
+// decode FC2 (K = I, a few super-steps): two 64-row blocks per workgroup, measured
+// faster than one (0.168 -> 0.163 ms for the 8-token layer's grouped GEMM)
+constexpr int kStreamFc2Blocks = 2;
+
 template <bool kActFP4, int kMode, bool kYBF16>
 static void launch_stream_mt(const GemmArgs& a, int mt, dim3 grid, hipStream_t stream) {
   switch (mt) {
-    case 1: gemm_stream1_kernel<kActFP4, kMode, kYBF16><<<grid, 256, 0, stream>>>(a); break;
+    case 1:
+      if constexpr (kMode == kModeFC2 && kStreamFc2Blocks == 2) {
+        // two 64-row blocks per workgroup (K = I is short: one super-step per wave per block)
+        grid.x = (unsigned)cdiv(a.N, 128);
+        gemm_stream1_kernel<kActFP4, kMode, kYBF16, 2><<<grid, 256, 0, stream>>>(a);
+      } else {
+        gemm_stream1_kernel<kActFP4, kMode, kYBF16, 1><<<grid, 256, 0, stream>>>(a);
+      }
+      break;
     case 2: gemm_stream_kernel<kActFP4, kMode, kYBF16, 2><<<grid, 256, 0, stream>>>(a); break;
     case 3: gemm_stream_kernel<kActFP4, kMode, kYBF16, 3><<<grid, 256, 0, stream>>>(a); break;
     default: gemm_stream_kernel<kActFP4, kMode, kYBF16, 4><<<grid, 256, 0, stream>>>(a); break;

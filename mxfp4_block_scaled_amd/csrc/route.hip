@@ -12,7 +12,8 @@
 // is a popcount over a 64-bit ballot-style mask of the tokens that chose e
 // (built with LDS atomic ORs); across waves and blocks it is a prefix count.
 //
-// Small T (<= 256): one workgroup does everything in one launch.
+// Small T (<= 256): one workgroup does everything in one launch (4 waves and one
+// token mask per expert for T <= 64, E <= 256).
 // Larger T: five launches - top-k (a group of 16 or 64 lanes per token),
 // per-block expert counts, per-expert scan over blocks, ranks -> pair_row,
 // and the inversion pair_row -> sorted_pair. The per-block counts live in sorted_pair (used as
@@ -189,6 +190,62 @@ __global__ void __launch_bounds__(kSmallThreads) route_small_kernel(
   }
 }
 
+// T <= 64 and E <= 256 (decode): the same steps with 4 waves and one 64-bit token
+// mask per expert
+constexpr int kTinyT = 64, kTinyE = 256, kTinyThreads = 256;
+
+__global__ void __launch_bounds__(kTinyThreads) route_tiny_kernel(
+    const float* __restrict__ logits, int T, int E, int topk, int32_t* __restrict__ topk_ids,
+    float* __restrict__ gates, int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ pair_row) {
+  constexpr int L = 16, TPW = 64 / L, NW = kTinyThreads / 64;
+  __shared__ unsigned long long bits[kTinyE];  // bit t: token t chose expert e
+  __shared__ int sids[kTinyT * 8];
+  __shared__ int offs[kTinyE + 1];
+  __shared__ int tmp[NW];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid < E) bits[tid] = 0ull;
+  const int grp = w * TPW + lane / L;
+  for (int t0 = 0; t0 < T; t0 += NW * TPW) {
+    const int t = t0 + grp;
+    const bool active = t < T;
+    float val[8];
+    int id[8];
+    group_topk<L>(logits + (int64_t)(active ? t : 0) * E, E, topk, active, val, id);
+    if (active && (lane & (L - 1)) == 0) {
+      write_route(t, topk, val, id, topk_ids, gates);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < topk) sids[t * topk + j] = id[j];
+    }
+  }
+  __syncthreads();
+  if (tid < T)
+    for (int j = 0; j < topk; ++j) atomicOr(&bits[sids[tid * topk + j]], 1ull << tid);
+  __syncthreads();
+  const int c = tid < E ? __popcll(bits[tid]) : 0;
+  int total;
+  const int base = block_exclusive_scan<NW>(c, tmp, &total);
+  if (tid < E) {
+    offs[tid] = base;
+    expert_offsets[tid] = base;
+  }
+  if (tid == 0) {
+    offs[E] = total;
+    expert_offsets[E] = total;
+  }
+  __syncthreads();
+  if (tid < T) {
+    for (int j = 0; j < topk; ++j) {
+      const int e = sids[tid * topk + j];
+      const int r = offs[e] + __popcll(bits[e] & ((1ull << tid) - 1ull));
+      const int p = tid * topk + j;
+      pair_row[p] = r;
+      sorted_pair[r] = p;
+    }
+  }
+}
+
 // large T, launch 1: top-k, one token per group of L lanes (64 / L tokens per wave)
 template <int L>
 __global__ void __launch_bounds__(kRouteThreads) route_topk_kernel(const float* __restrict__ logits, int64_t T,
@@ -317,6 +374,11 @@ template <int L>
 static void launch_route_l(const float* logits, int64_t T, int E, int topk, int32_t* topk_ids, float* gates,
                            int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_row, hipStream_t stream) {
   const size_t bits_bytes = sizeof(unsigned long long) * 4 * E;
+  if (L == 16 && T <= kTinyT && E <= kTinyE) {
+    route_tiny_kernel<<<1, kTinyThreads, 0, stream>>>(logits, (int)T, E, topk, topk_ids, gates, expert_offsets,
+                                                      sorted_pair, pair_row);
+    return;
+  }
   if (T <= kSmallT) {
     route_small_kernel<L><<<1, kSmallThreads, bits_bytes, stream>>>(logits, (int)T, E, topk, topk_ids, gates,
                                                                      expert_offsets, sorted_pair, pair_row);
