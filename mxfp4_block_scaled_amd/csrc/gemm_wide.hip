@@ -250,7 +250,10 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
   __shared__ WideScales scl0, scl1;
   __shared__ WideSlot slot0, slot1;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  // the wave index through readfirstlane: the compiler then sees it as uniform and
+  // forms the LDS-DMA destinations (M0) in scalar registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5,
+            r32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;  // rows [64 wm, 64 wm + 64), column half wn
 
   const int ntiles = a.ntiles;
