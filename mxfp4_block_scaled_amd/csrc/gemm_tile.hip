@@ -46,7 +46,9 @@ __global__ void __launch_bounds__(256) gemm_tile4_kernel(GemmArgs a) {
   constexpr int kFA = kActFP4 ? kFmtFP4 : kFmtFP8;
   __shared__ T4Slot<kActFP4> slot0, slot1, slot2, slot3;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  // wave index through readfirstlane: seen as uniform, LDS-DMA destinations stay scalar
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5,
+            r32 = lane & 31;
 
   // XCD-aware order (block b runs on XCD b % 8): XCD x owns n-tiles [x*nt/8, (x+1)*nt/8)
   const int ntiles = a.ntiles;
