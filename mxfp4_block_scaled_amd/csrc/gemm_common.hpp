@@ -96,6 +96,20 @@ __device__ __forceinline__ void find_unit(const int32_t* __restrict__ off, int E
   loc_out = __shfl(loc, src);
 }
 
+// the value of lane l ^ 32 (a swap of the wave's halves): gfx950's
+// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes 0..31 of
+// its second, on the VALU (no LDS round trip); with both operands x, the first
+// result holds x of lane l - 32 in the upper half, the second x of lane l + 32 in
+// the lower half
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (threadIdx.x & 32u) ? r[0] : r[1];
+#else
+  return x;
+#endif
+}
+
 // silu(g) * u with the hardware exponential and reciprocal (about 1 ulp each)
 __device__ __forceinline__ float silu_mul(float g, float u) {
 #if defined(__HIP_DEVICE_COMPILE__)

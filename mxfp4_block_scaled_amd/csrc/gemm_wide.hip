@@ -28,7 +28,7 @@ constexpr int SG = G * SB;               // scale bytes per row per group
 constexpr int IA = BM * CH / 64 / 8;     // A copies (16 B per lane) per wave per stage
 constexpr int IB = BN * CH / 64 / 8;     // B copies per wave per stage
 constexpr int D = IA + IB;
-constexpr int STG = 4352;                // FC2 / dense epilogue staging bytes per wave
+constexpr int STG = 4352;                // fp32 epilogue staging bytes per wave (bf16: 8192)
 }  // namespace wide
 
 struct alignas(16) WideSlot {
@@ -41,7 +41,8 @@ struct alignas(16) WideScales {
   uint8_t B[wide::BN * wide::SG];
 };
 static_assert(2 * sizeof(WideSlot) + 2 * sizeof(WideScales) <= 160 * 1024, "ring and scale buffers must fit in LDS");
-static_assert(8 * wide::STG <= (int)sizeof(WideSlot), "eight waves' staging regions must fit one slot");
+static_assert(8 * wide::STG <= (int)sizeof(WideSlot) && 8 * 8192 <= (int)sizeof(WideSlot),
+              "eight waves' staging regions must fit one slot");
 
 #ifndef MXF_WIDE_ORDER
 #define MXF_WIDE_ORDER 1
@@ -114,14 +115,17 @@ __device__ __forceinline__ void wide_work_item(const int32_t* __restrict__ off, 
 // + 4 (l / 32) + v % 4: every lane holds runs of 4 consecutive columns of one row.
 // FC1: h = silu(gate) * up, requantised to E2M1 per 32 I-columns - a block is one
 // fragment's 32 columns of one row, held half by lane l and half by lane l ^ 32;
-// FC2 / dense: y or c in bf16 or fp32, staged 16 (bf16) or 8 (fp32) rows at a time
-// in the wave's 4352-byte LDS region stg (8- or 16-byte runs in, 16-byte row pieces
-// out, so each store instruction writes whole 256- or 512-byte row segments).
+// FC2 / dense: y or c in bf16 or fp32 through LDS - bf16 a whole fragment (32 rows)
+// at a time in the wave's 8 KB of the slot, fp32 8 rows at a time in a 4352-byte
+// region (8- or 16-byte runs in, 16-byte row pieces out, so each store instruction
+// writes whole 256- or 512-byte row segments).
 template <int kMode, bool kYBF16>
-__device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&acc)[2][4], uint8_t* stg, int n_tile,
+__device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&acc)[2][4], uint8_t* slot, int n_tile,
                                               int64_t row0, int m) {
   using namespace wide;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5, r32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 5,
+            r32 = lane & 31;
+  uint8_t* const stg = slot + wave * STG;
   const int wm = wave >> 1, wn = wave & 1;
   if (64 * wm >= m) return;
 #pragma unroll
@@ -139,7 +143,7 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&ac
           h[v] = silu_mul(acc[fm][f][v], acc[fm][f + 2][v]);
           amax = max(amax, __float_as_uint(h[v]) & 0x7FFFFFFFu);
         }
-        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+        amax = max(amax, lane_xor32(amax));
         const uint32_t byte = scale_byte_from_amax_bits(amax, kEmaxE2M1);
         // E2M1 codes by the hardware conversion (equal to e2m1_code; small scale
         // bytes lifted by 2^64 as in quantize_block32)
@@ -159,7 +163,7 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&ac
 #endif
           c[q] = w;
         }
-        const uint32_t p0 = (uint32_t)__shfl_xor((int)c[0], 32), p1 = (uint32_t)__shfl_xor((int)c[1], 32);
+        const uint32_t p0 = lane_xor32(c[0]), p1 = lane_xor32(c[1]);
         // the block's 16 bytes: 2-byte runs in column order, lane g = 0's run j, then lane 1's
         if (g == 0 && ok) {
           const int64_t icol = (int64_t)n_tile * (BN / 2) + 64 * wn + 32 * f;
@@ -170,36 +174,38 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&ac
         }
       }
     } else if (kYBF16) {
-      uint16_t(*ob)[136] = reinterpret_cast<uint16_t(*)[136]>(stg);  // 16 x 136 x 2 = 4352 bytes
+      // the fragment's 32 rows x 128 columns at once in the wave's 8 KB of slot 1:
+      // row r at 256 r, 16-byte piece p at piece p ^ (r % 16), and its two 8-byte
+      // halves swapped for r >= 16, so that the 8-byte writes (32 rows of one piece
+      // per half-wave) and the 16-byte reads (one row per 16 lanes) both spread over
+      // all 64 banks
+      uint8_t* const ob = slot + wave * 8192;
       uint16_t* out = static_cast<uint16_t*>(a.out);
       const int64_t col0 = (int64_t)n_tile * BN + 128 * wn;
+      const int hs = (r32 >> 4) & 1;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {  // rows r32 in [16 hh, 16 hh + 16)
-        if ((r32 >> 4) == hh) {
+      for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
-          for (int fn = 0; fn < 4; ++fn)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const __bf16 b0 = (__bf16)acc[fm][fn][4 * j], b1 = (__bf16)acc[fm][fn][4 * j + 1];
-              const __bf16 b2 = (__bf16)acc[fm][fn][4 * j + 2], b3 = (__bf16)acc[fm][fn][4 * j + 3];
-              uint2 d;
-              d.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-              d.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-              *reinterpret_cast<uint2*>(&ob[r32 & 15][32 * fn + 8 * j + 4 * g]) = d;
-            }
+        for (int j = 0; j < 4; ++j) {
+          const __bf16 b0 = (__bf16)acc[fm][fn][4 * j], b1 = (__bf16)acc[fm][fn][4 * j + 1];
+          const __bf16 b2 = (__bf16)acc[fm][fn][4 * j + 2], b3 = (__bf16)acc[fm][fn][4 * j + 3];
+          uint2 d;
+          d.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+          d.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+          *reinterpret_cast<uint2*>(ob + 256 * r32 + 16 * ((4 * fn + j) ^ (r32 & 15)) + 8 * (g ^ hs)) = d;
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {  // 16 rows x 128 columns = 256 pieces of 16 bytes
-          const int idx = lane + 64 * j;
-          const int rr = idx >> 4, c8 = idx & 15;
-          const int lrow = 64 * wm + 32 * fm + 16 * hh + rr;
-          if (lrow < m)  // y is read once, by the combine: non-temporal stores
-            __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(&ob[rr][8 * c8]),
-                                        reinterpret_cast<v4i*>(out + (row0 + lrow) * a.N + col0 + 8 * c8));
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      for (int k = 0; k < 8; ++k) {  // 32 rows x 16 pieces of 16 bytes
+        const int idx = lane + 64 * k;
+        const int rr = idx >> 4, c = idx & 15;
+        const int lrow = 64 * wm + 32 * fm + rr;
+        v4i v = *reinterpret_cast<const v4i*>(ob + 256 * rr + 16 * (c ^ (rr & 15)));
+        if (rr & 16) v = v4i{v[2], v[3], v[0], v[1]};
+        if (lrow < m)  // y is read once, by the combine: non-temporal stores
+          __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(out + (row0 + lrow) * a.N + col0 + 8 * c));
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     } else {
       float(*of)[132] = reinterpret_cast<float(*)[132]>(stg);  // 8 x 132 x 4 = 4224 bytes
       float* out = static_cast<float*>(a.out);
@@ -508,7 +514,7 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
     if (kMode != kModeFC1 || (more_tiles && ngrp % 2 == 1)) lds_barrier();  // every wave is done with the ring
     if (more_tiles && ngrp % 2 == 1) issue_scales(scl0, 0, t + 1);
     // staging (FC2 / dense) in slot 1 only: slot 0 may be receiving the next n-tile's stage 0
-    wide_epilogue<kMode, kYBF16>(a, acc, reinterpret_cast<uint8_t*>(&slot1) + wave * STG, n_tile + t, row0, m);
+    wide_epilogue<kMode, kYBF16>(a, acc, reinterpret_cast<uint8_t*>(&slot1), n_tile + t, row0, m);
   });
 }
 

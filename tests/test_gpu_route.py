@@ -39,7 +39,10 @@ def test_route_sizes_across_the_small_and_multi_block_paths(T):
     _check(dg.logits(100 + T, T, 256, "normal"), 6)
 
 
-@pytest.mark.parametrize("T,E,k", [(50, 8, 3), (700, 16, 8), (300, 64, 1), (5, 6, 6), (900, 1024, 8)])
+@pytest.mark.parametrize("T,E,k", [(50, 8, 3), (700, 16, 8), (300, 64, 1), (5, 6, 6), (900, 1024, 8),
+                                   (40, 512, 8),   # T <= 64 with E > 256: the general small-T kernel
+                                   (64, 256, 8),   # the 4-wave kernel at its largest T and E
+                                   (33, 300, 6)])  # E not a multiple of 16 lanes
 def test_route_ties_and_other_shapes(T, E, k):
     g = np.random.default_rng(T + E + k)
     logits = g.integers(-2, 3, (T, E)).astype(np.float32)  # many exact ties
