@@ -298,9 +298,21 @@ static void launch_tile4(const GemmArgs& a, int64_t m_units, hipStream_t stream)
   const int64_t nn = cdiv(a.ntiles, 8);
   const dim3 grid((unsigned)(8 * nn * m_units));
   const int64_t nst = a.K / 256;
-  if (nst == 28) gemm_tile4_kernel<kActFP4, kMode, kYBF16, 28><<<grid, 256, 0, stream>>>(a);
-  else if (nst == 8) gemm_tile4_kernel<kActFP4, kMode, kYBF16, 8><<<grid, 256, 0, stream>>>(a);
-  else gemm_tile4_kernel<kActFP4, kMode, kYBF16, 0><<<grid, 256, 0, stream>>>(a);
+  // Fully unrolled instances for K = 7168 and 2048 where they fit the registers:
+  // with fp32 outputs (dense C, FC2 with fp32 y) they would spill about 200 VGPRs,
+  // so those take the loop instance (no spills).
+  constexpr bool kUnroll = kMode == kModeFC1 || (kMode == kModeFC2 && kYBF16);
+  if constexpr (kUnroll) {
+    if (nst == 28) {
+      gemm_tile4_kernel<kActFP4, kMode, kYBF16, 28><<<grid, 256, 0, stream>>>(a);
+      return;
+    }
+    if (nst == 8) {
+      gemm_tile4_kernel<kActFP4, kMode, kYBF16, 8><<<grid, 256, 0, stream>>>(a);
+      return;
+    }
+  }
+  gemm_tile4_kernel<kActFP4, kMode, kYBF16, 0><<<grid, 256, 0, stream>>>(a);
 }
 
 // Measured on the 2048- and 16384-token layers: with FP8 activations the

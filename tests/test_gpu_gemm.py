@@ -37,6 +37,8 @@ def test_dense_workloads(name):
     # M <= 64 with more than 4 super-steps of 512 k: K split into slices summed in a fixed order
     (33, 48, 5120, "e2m1"),   # 3 slices, the last with 2 super-steps (two idle waves)
     (64, 96, 2560, "e4m3"),   # 2 slices, the last with 1 super-step
+    # E4M3 activations, M > 64, N % 256 == 0 at the layer's K values (fp32 C: the loop instance)
+    (130, 256, 7168, "e4m3"), (100, 512, 2048, "e4m3"),
 ])
 def test_dense_ragged_shapes(M, N, K, fmt):
     a = dg.activations(M * 7 + N, M, K, outliers=True)

@@ -96,6 +96,17 @@ def test_layer_fp32_y():
     _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e4m3")
 
 
+def test_layer_fp32_y_fp8_tiles():
+    # FP8 activations past 64 tokens: register-streamed tiles, FC2 with fp32 y and K = I = 2048
+    T, H, I, E, k = 200, 1024, 2048, 8, 3
+    x = dg.activations(14, T, H)
+    logits = dg.logits(14, T, E, "normal")
+    w1, s1, w2, s2 = dg.moe_weights(14, E, H, I, 120, 128)
+    g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, "e4m3", y_dtype=torch.float32)
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e4m3")
+    _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e4m3")
+
+
 def test_layer_fp32_y_fp4_tiles():
     T, H, I, E, k = 300, 1024, 512, 8, 4
     x = dg.activations(13, T, H)
