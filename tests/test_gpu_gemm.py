@@ -39,6 +39,7 @@ def test_dense_workloads(name):
     (64, 96, 2560, "e4m3"),   # 2 slices, the last with 1 super-step
     # E4M3 activations, M > 64, N % 256 == 0 at the layer's K values (fp32 C: the loop instance)
     (130, 256, 7168, "e4m3"), (100, 512, 2048, "e4m3"),
+    (260, 256, 7168, "e2m1"),  # E2M1, 256 x 256 tiles, K = 7168 (fully unrolled stages), 4-row tail unit
 ])
 def test_dense_ragged_shapes(M, N, K, fmt):
     a = dg.activations(M * 7 + N, M, K, outliers=True)

@@ -65,6 +65,7 @@ def _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt, rows=None, tokens=None):
     (65, 512, 512, 4, 2, "e4m3", 4),       # just past the streaming threshold
     (700, 2048, 512, 4, 2, "e2m1", 5),     # FP4 x FP4, ~350 rows per expert: full and partial 256-row units
     (300, 1024, 2048, 8, 2, "e2m1", 6),    # FP4 FC2 with K = 2048: four n-tiles per workgroup
+    (12, 1024, 2048, 16, 6, "e2m1", 7),    # FP4 decode: one-fragment kernels, FC2 two row blocks per workgroup
 ])
 def test_layer_small_shapes_full_oracle(T, H, I, E, k, fmt, seed):
     x = dg.activations(seed, T, H)
@@ -86,8 +87,9 @@ def test_layer_skewed_routing_one_expert_takes_all():
     _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e4m3")
 
 
-def test_layer_fp32_y():
-    T, H, I, E, k = 24, 512, 512, 8, 3
+@pytest.mark.parametrize("T", [24, 10])  # two 16-row fragments / one (FC2 with two row blocks)
+def test_layer_fp32_y(T):
+    H, I, E, k = 512, 512, 8, 3
     x = dg.activations(12, T, H)
     logits = dg.logits(12, T, E, "normal")
     w1, s1, w2, s2 = dg.moe_weights(12, E, H, I, 120, 128)
@@ -107,8 +109,9 @@ def test_layer_fp32_y_fp8_tiles():
     _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e4m3")
 
 
-def test_layer_fp32_y_fp4_tiles():
-    T, H, I, E, k = 300, 1024, 512, 8, 4
+@pytest.mark.parametrize("I", [512, 2048])  # FC2 stage loop / four chained n-tiles (K = 2048)
+def test_layer_fp32_y_fp4_tiles(I):
+    T, H, E, k = 300, 1024, 8, 4
     x = dg.activations(13, T, H)
     logits = dg.logits(13, T, E, "normal")
     w1, s1, w2, s2 = dg.moe_weights(13, E, H, I, 120, 128)
