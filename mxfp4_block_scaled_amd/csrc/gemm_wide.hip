@@ -44,10 +44,6 @@ static_assert(2 * sizeof(WideSlot) + 2 * sizeof(WideScales) <= 160 * 1024, "ring
 static_assert(8 * wide::STG <= (int)sizeof(WideSlot) && 8 * 8192 <= (int)sizeof(WideSlot),
               "eight waves' staging regions must fit one slot");
 
-#ifndef MXF_WIDE_ORDER
-#define MXF_WIDE_ORDER 1
-#endif
-
 // Work item of block j on XCD x for the grouped GEMMs. Items run expert by expert;
 // within an expert, n-tile by n-tile, and within an n-tile over the expert's units,
 // so the workgroups resident on one XCD at a time cover one or two experts: each
@@ -269,7 +265,7 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
   int e = 0, n_tile;
   int64_t row0;
   int m;
-  if (kMode == kModeDense || !MXF_WIDE_ORDER) {
+  if (kMode == kModeDense) {
     // XCD x owns n-tiles [x*nt/8, (x+1)*nt/8) and walks the row units
     const int n_lo = x * ntiles / 8, n_hi = (x + 1) * ntiles / 8, nn = n_hi - n_lo;
     if (nn == 0) return;
@@ -539,24 +535,14 @@ static void launch_wide_t(const GemmArgs& a, int64_t m_units, hipStream_t stream
 }
 
 // Measured on the 16384-token FP4 layer: four n-tiles per workgroup take FC2 (8
-// stages per n-tile) from 1.41 to 1.30 ms; FC1 (28 stages) gains nothing from two,
-// whose unrolled code is twice the size, so it keeps one.
-#ifndef MXF_WIDE_NG_FC2
-#define MXF_WIDE_NG_FC2 4
-#endif
-
+// stages per n-tile) from 1.41 to 1.30 ms (seven: no further change); FC1 (28
+// stages) gains nothing from two, so it keeps one.
 void launch_wide_gemm(int mode, bool y_bf16, const GemmArgs& a_in, int64_t m_units, hipStream_t stream) {
-  // consecutive n-tiles per workgroup for the grouped GEMMs: the ring runs on from
-  // one n-tile into the next, which needs an even stage count
+  // consecutive n-tiles per workgroup for the grouped FC2 at K = 2048: the ring runs
+  // on from one n-tile into the next, which needs an even stage count
   GemmArgs a = a_in;
   a.ngroup = 1;
-  if (MXF_WIDE_ORDER && mode == kModeFC2 && a.K / wide::KS == 8) {
-    for (int ng = MXF_WIDE_NG_FC2; ng > 1; ng /= 2)
-      if (a.ntiles % ng == 0 && (ng == 4 || ng == 2)) {
-        a.ngroup = ng;
-        break;
-      }
-  }
+  if (mode == kModeFC2 && a.K / wide::KS == 8) a.ngroup = a.ntiles % 4 == 0 ? 4 : a.ntiles % 2 == 0 ? 2 : 1;
   if (mode == kModeFC1) launch_wide_t<kModeFC1, false>(a, m_units, stream);
   else if (mode == kModeDense) launch_wide_t<kModeDense, false>(a, m_units, stream);
   else if (y_bf16) launch_wide_t<kModeFC2, true>(a, m_units, stream);
