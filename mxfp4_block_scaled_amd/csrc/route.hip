@@ -31,6 +31,14 @@ __device__ __forceinline__ bool beats(float x, int i, float y, int j) {
   return i >= 0 && (j < 0 || x > y || (x == y && i < j));
 }
 
+// the (value, index) pair of the lane that DPP control kCtrl selects (all lanes active)
+template <int kCtrl, typename F>
+__device__ __forceinline__ void take_dpp(float bv, int bi, F&& take) {
+  const int ov = __builtin_amdgcn_update_dpp(0, __float_as_int(bv), kCtrl, 0xF, 0xF, false);
+  const int oi = __builtin_amdgcn_update_dpp(0, bi, kCtrl, 0xF, 0xF, false);
+  take(__int_as_float(ov), oi);
+}
+
 // Top-k of one logits row by a group of L lanes (L = 16 or 64; 64 / L tokens per
 // wave). Lane j of the group holds logits e = j + L*i, i < 16 (E <= 16 L). Each
 // of the k rounds takes the group's best not-yet-taken (logit, index) pair with
@@ -64,15 +72,22 @@ __device__ __forceinline__ void group_topk(const float* __restrict__ row, int E,
           bi = e;
         }
       }
-#pragma unroll
-      for (int d = L / 2; d >= 1; d >>= 1) {
-        const float ov = __shfl_xor(bv, d);
-        const int oi = __shfl_xor(bi, d);
+      // the group's best pair: a max over a total order, so any exchange pattern that
+      // reaches all L lanes will do - within each 16-lane row by DPP on the VALU
+      // (swap neighbours, swap pairs, mirror each 8-lane half, mirror the row), across
+      // rows (L = 64) by lane permutes
+      auto take = [&](float ov, int oi) {
         if (beats(ov, oi, bv, bi)) {
           bv = ov;
           bi = oi;
         }
-      }
+      };
+      take_dpp<0xB1>(bv, bi, take);   // quad_perm [1, 0, 3, 2]
+      take_dpp<0x4E>(bv, bi, take);   // quad_perm [2, 3, 0, 1]
+      take_dpp<0x141>(bv, bi, take);  // row_half_mirror
+      take_dpp<0x140>(bv, bi, take);  // row_mirror
+#pragma unroll
+      for (int d = 16; d < L; d <<= 1) take(__shfl_xor(bv, d), __shfl_xor(bi, d));
       if (bi >= 0 && (bi & (L - 1)) == j) taken |= 1u << (bi / L);
       val[r] = bv;
       id[r] = bi;
