@@ -43,8 +43,8 @@ BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,
 # passes, scaled by a 1 GiB copy (2.0 x FETCH_SIZE + 1.0 x WRITE_SIZE; the passes and the
 # calibration are in profiles/moe_layer_hbm_traffic.md). They hold only for the GEMM sources
 # they were measured on (sha-256 over GEMM_SOURCES): on any other source traffic = null.
-TRAFFIC_SRC_SHA256 = "23946a42bec94a5e70c7a25291dede6a8a0003e2dd99c542050f2b221b839f02"
-TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8796492816, "moe_decode_t8": 1008469450}
+TRAFFIC_SRC_SHA256 = "f86a36b5165346f258c1e327b3c61c2d18b7aa93478b33385a170285e06f55bb"
+TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8791438656, "moe_decode_t8": 1008454147}
 
 
 GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "mx_codec.hpp")
