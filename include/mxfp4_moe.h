@@ -54,7 +54,7 @@ typedef enum {
   MXF_ERR_SHAPE = 2,       /* a size is negative, or not a multiple the kernels need */
   MXF_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
   MXF_ERR_FORMAT = 4,      /* unknown element format or dtype enum */
-  MXF_ERR_UNSUPPORTED = 5, /* valid arguments outside the sizes this build handles */
+  MXF_ERR_UNSUPPORTED = 5, /* valid arguments outside the sizes this library handles */
   MXF_ERR_LAUNCH = 6,      /* a kernel launch failed (hipGetLastError) */
   MXF_ERR_WORKSPACE = 7    /* workspace missing or smaller than required */
 } mxf_status;

@@ -31,7 +31,7 @@ const char* mxf_status_str(int status) {
     case MXF_ERR_SHAPE: return "MXF_ERR_SHAPE: a size is negative or not a multiple the kernels need";
     case MXF_ERR_ALIGN: return "MXF_ERR_ALIGN: a pointer is not 16-byte aligned";
     case MXF_ERR_FORMAT: return "MXF_ERR_FORMAT: unknown element format or dtype";
-    case MXF_ERR_UNSUPPORTED: return "MXF_ERR_UNSUPPORTED: sizes outside what this build handles";
+    case MXF_ERR_UNSUPPORTED: return "MXF_ERR_UNSUPPORTED: sizes outside what this library handles";
     case MXF_ERR_LAUNCH: return "MXF_ERR_LAUNCH: a kernel launch failed";
     case MXF_ERR_WORKSPACE: return "MXF_ERR_WORKSPACE: workspace missing or too small";
     default: return "unknown mxf_status";

@@ -1,4 +1,4 @@
-"""The straddle rule (tests/helpers.py) that judges the GPU's requantised h codes,
+"""The straddle rule (tests/helpers.py) that decides on the GPU's requantised h codes,
 checked on the CPU with planted codes: it accepts the oracle's own codes and
 mismatches that fp32 accumulation can explain (a value within tol of the block
 amax from the other side of a rounding boundary, including several subnormal
