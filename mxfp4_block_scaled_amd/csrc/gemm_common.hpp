@@ -110,6 +110,67 @@ __device__ __forceinline__ uint32_t lane_xor32(uint32_t x) {
 #endif
 }
 
+// Work item of block j on XCD x for the grouped GEMMs (units of BM rows). Items run expert by expert;
+// within an expert, n-tile by n-tile, and within an n-tile over the expert's units,
+// so the workgroups resident on one XCD at a time cover one or two experts: each
+// activation unit is shared by every n-tile there and each weight tile by the
+// expert's units, and L2 holds both. The U * ntiles items are split into 8
+// contiguous ranges, one per XCD (block b runs on XCD b % 8). Called by a whole
+// wave; the results are wave-uniform. e_out < 0: no item for this block.
+template <int BM>
+__device__ __forceinline__ void grouped_work_item(const int32_t* __restrict__ off, int E, int ntiles, int x, int j,
+                                                  int& e_out, int& n_out, int& loc_out) {
+  const int lane = threadIdx.x & 63;
+  const int C = (E + 63) >> 6;
+  const int first = lane * C;
+  int units = 0;
+  for (int i = 0; i < C; ++i) {
+    const int e = first + i;
+    if (e < E) units += units_of<BM>(off[e + 1] - off[e]);
+  }
+  int incl = units;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  const int excl = incl - units;
+  const int64_t total = (int64_t)__shfl(incl, 63) * ntiles;
+  const int64_t w = x * total / 8 + j;
+  e_out = -1;
+  n_out = loc_out = 0;
+  if (w >= (x + 1) * total / 8) return;
+  const int p = (int)(w / ntiles);  // a unit of the wanted expert
+  const bool mine = p >= excl && p < incl;
+  const unsigned long long msk = __ballot(mine);
+  if (msk == 0) return;
+  const int src = __ffsll((long long)msk) - 1;
+  int ee = -1, ue = 0, ke = 1;
+  if (mine) {
+    int acc = excl;
+    for (int i = 0; i < C; ++i) {
+      const int e = first + i;
+      if (e < E) {
+        const int n = units_of<BM>(off[e + 1] - off[e]);
+        if (p < acc + n) {
+          ee = e;
+          ue = acc;
+          ke = n;
+          break;
+        }
+        acc += n;
+      }
+    }
+  }
+  ee = __shfl(ee, src);
+  ue = __shfl(ue, src);
+  ke = __shfl(ke, src);
+  const int64_t local = w - (int64_t)ue * ntiles;
+  e_out = ee;
+  n_out = (int)(local / ke);
+  loc_out = (int)(local % ke);
+}
+
 // silu(g) * u with the hardware exponential and reciprocal (about 1 ulp each)
 __device__ __forceinline__ float silu_mul(float g, float u) {
 #if defined(__HIP_DEVICE_COMPILE__)

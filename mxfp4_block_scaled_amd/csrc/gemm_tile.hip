@@ -50,24 +50,26 @@ __global__ void __launch_bounds__(256) gemm_tile4_kernel(GemmArgs a) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5,
             r32 = lane & 31;
 
-  // XCD-aware order (block b runs on XCD b % 8): XCD x owns n-tiles [x*nt/8, (x+1)*nt/8)
+  // XCD-aware order (block b runs on XCD b % 8). Dense: XCD x owns n-tiles
+  // [x*nt/8, (x+1)*nt/8) and walks the row units. Grouped: expert-major items split
+  // into one contiguous range per XCD, so an XCD's resident workgroups share
+  // activation units and weight tiles in its L2.
   const int ntiles = a.ntiles;
   const int x = (int)(blockIdx.x & 7u), jb = (int)(blockIdx.x >> 3);
-  const int n_lo = x * ntiles / 8, n_hi = (x + 1) * ntiles / 8, nn = n_hi - n_lo;
-  if (nn == 0) return;
-  const int m_unit = jb / nn;
-  const int n_tile = n_lo + jb % nn;
-
-  int e = 0;
+  int e = 0, n_tile;
   int64_t row0;
   int m;
   if (kMode == kModeDense) {
+    const int n_lo = x * ntiles / 8, n_hi = (x + 1) * ntiles / 8, nn = n_hi - n_lo;
+    if (nn == 0) return;
+    const int m_unit = jb / nn;
+    n_tile = n_lo + jb % nn;
     row0 = (int64_t)m_unit * BM;
     if (row0 >= a.M) return;
     m = (int)(a.M - row0 < BM ? a.M - row0 : BM);
   } else {
     int loc;
-    find_unit<BM>(a.offsets, a.E, m_unit, e, loc);
+    grouped_work_item<BM>(a.offsets, a.E, ntiles, x, jb, e, n_tile, loc);
     if (e < 0) return;
     row0 = a.offsets[e] + (int64_t)loc * BM;
     m = min(BM, a.offsets[e + 1] - (int)row0);

@@ -44,67 +44,6 @@ static_assert(2 * sizeof(WideSlot) + 2 * sizeof(WideScales) <= 160 * 1024, "ring
 static_assert(8 * wide::STG <= (int)sizeof(WideSlot) && 8 * 8192 <= (int)sizeof(WideSlot),
               "eight waves' staging regions must fit one slot");
 
-// Work item of block j on XCD x for the grouped GEMMs. Items run expert by expert;
-// within an expert, n-tile by n-tile, and within an n-tile over the expert's units,
-// so the workgroups resident on one XCD at a time cover one or two experts: each
-// activation unit is shared by every n-tile there and each weight tile by the
-// expert's units, and L2 holds both. The U * ntiles items are split into 8
-// contiguous ranges, one per XCD (block b runs on XCD b % 8). Called by a whole
-// wave; the results are wave-uniform. e_out < 0: no item for this block.
-__device__ __forceinline__ void wide_work_item(const int32_t* __restrict__ off, int E, int ntiles, int x, int j,
-                                               int& e_out, int& n_out, int& loc_out) {
-  constexpr int BM = wide::BM;
-  const int lane = threadIdx.x & 63;
-  const int C = (E + 63) >> 6;
-  const int first = lane * C;
-  int units = 0;
-  for (int i = 0; i < C; ++i) {
-    const int e = first + i;
-    if (e < E) units += units_of<BM>(off[e + 1] - off[e]);
-  }
-  int incl = units;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
-  }
-  const int excl = incl - units;
-  const int64_t total = (int64_t)__shfl(incl, 63) * ntiles;
-  const int64_t w = x * total / 8 + j;
-  e_out = -1;
-  n_out = loc_out = 0;
-  if (w >= (x + 1) * total / 8) return;
-  const int p = (int)(w / ntiles);  // a unit of the wanted expert
-  const bool mine = p >= excl && p < incl;
-  const unsigned long long msk = __ballot(mine);
-  if (msk == 0) return;
-  const int src = __ffsll((long long)msk) - 1;
-  int ee = -1, ue = 0, ke = 1;
-  if (mine) {
-    int acc = excl;
-    for (int i = 0; i < C; ++i) {
-      const int e = first + i;
-      if (e < E) {
-        const int n = units_of<BM>(off[e + 1] - off[e]);
-        if (p < acc + n) {
-          ee = e;
-          ue = acc;
-          ke = n;
-          break;
-        }
-        acc += n;
-      }
-    }
-  }
-  ee = __shfl(ee, src);
-  ue = __shfl(ue, src);
-  ke = __shfl(ke, src);
-  const int64_t local = w - (int64_t)ue * ntiles;
-  e_out = ee;
-  n_out = (int)(local / ke);
-  loc_out = (int)(local % ke);
-}
-
 // Epilogue of one 256 x 256 tile, straight from the accumulators (no LDS). The
 // MFMAs take the weight fragment as their first operand, so acc[fm][fn][v] of
 // lane l is token row 64 wm + 32 fm + l % 32 and output column c(fn) + 8 (v / 4)
@@ -284,7 +223,7 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
     }
   } else {
     int loc, n_grp;
-    wide_work_item(a.offsets, a.E, ntiles / ntg, x, jb, e, n_grp, loc);
+    grouped_work_item<BM>(a.offsets, a.E, ntiles / ntg, x, jb, e, n_grp, loc);
     if (e < 0) return;
     n_tile = n_grp * ntg;
     row0 = a.offsets[e] + (int64_t)loc * BM;
