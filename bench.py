@@ -43,8 +43,8 @@ BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,
 # passes, scaled by a 1 GiB copy (2.0 x FETCH_SIZE + 1.0 x WRITE_SIZE; the passes and the
 # calibration are in profiles/moe_layer_hbm_traffic.md). They hold only for the GEMM sources
 # they were measured on (sha-256 over GEMM_SOURCES): on any other source traffic = null.
-TRAFFIC_SRC_SHA256 = "6fcec7efc469265fbb38e60ae8f4ccf107bfd50fa14f16355c04110d0a8f4baa"
-TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8718462016, "moe_decode_t8": 1008458470}
+TRAFFIC_SRC_SHA256 = "b02d4571c69b9c44676591f29c524ec621c5e9f9ab500ca4d15e90c500ae519a"
+TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8715523936, "moe_decode_t8": 1008555744}
 
 
 GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "mx_codec.hpp")

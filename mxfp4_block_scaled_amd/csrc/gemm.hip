@@ -4,6 +4,10 @@
 
 namespace mxf {
 
+// grouped GEMMs with few rows per expert: experts of at most this many rows (one 16-row
+// fragment) go to the weight-streaming kernel
+constexpr int kSplitRows = 16;
+
 int dense_ksplit(int64_t M, int64_t N, int64_t K) {
   // M <= 64 streams the weights with 64 weight rows per workgroup: N / 64 workgroups
   // fill the chip only for very wide N, so K is also split into slices of 4
@@ -93,6 +97,17 @@ int launch_grouped_gemm(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, 
     // R rows over at most `slots` non-empty experts, each of which adds at most one partial unit
     f1.ntiles = (int)(I / (tile::BN / 2));
     f2.ntiles = (int)(H / tile::BN);
+    // Fewer than 64 rows per expert on average (skewed routing): the experts of at most
+    // 16 rows stream their weights through the one-fragment kernel at HBM rate instead
+    // of each occupying a tile workgroup for a full weight tile; the tiled kernels take
+    // the rest. Both pairs of launches size their grids for every expert and skip the
+    // other class's.
+    const bool split = R < 64 * (int64_t)E;
+    if (split) {
+      f1.split = f2.split = kSplitRows;
+      launch_stream_gemm(kModeFC1, false, act_fp4, f1, 1, dim3((unsigned)(I / 32), (unsigned)slots), stream);
+      launch_stream_gemm(kModeFC2, y_bf16, act_fp4, f2, 1, dim3((unsigned)cdiv(H, 64), (unsigned)slots), stream);
+    }
     if (launch_tile_gemm(kModeFC1, false, act_fp4, f1, R, slots, stream)) return -1;
     if (launch_tile_gemm(kModeFC2, y_bf16, act_fp4, f2, R, slots, stream)) return -1;
   }

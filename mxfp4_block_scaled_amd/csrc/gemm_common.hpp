@@ -36,19 +36,24 @@ struct GemmArgs {
   int ntiles;  // tile kernel: weight-row tiles per expert (1-D grid: block = m_unit * ntiles + n_tile)
   int kchunk;  // dense weight-streaming kernel: 512-k super-steps per grid.y slice (0: the whole K)
   int ngroup;  // wide kernel, grouped GEMMs: consecutive n-tiles per workgroup (ntiles % ngroup == 0; 0: one)
+  int split;   // grouped GEMMs: experts with 1..split rows run in the streaming kernel, the
+               // others in the tiled kernels (0: every non-empty expert in the launched kernel)
 };
 
 // ---------------------------------------------------------------------------------
-// Which expert does work unit u belong to? units(e) = (count_e > 0) when BM == 0,
-// else ceil(count_e / BM). Called by a whole wave; results are wave-uniform.
+// Which expert does work unit u belong to? units(e) = (count_e > 0) when BM == 0 (the
+// streaming kernel), else ceil(count_e / BM); with split > 0 the streaming kernel
+// counts only experts of at most split rows and the tiled kernels only the others.
+// Called by a whole wave; results are wave-uniform.
 template <int BM>
-__device__ __forceinline__ int units_of(int c) {
-  if constexpr (BM == 0) return c > 0 ? 1 : 0;
-  else return (c + BM - 1) / BM;
+__device__ __forceinline__ int units_of(int c, int split) {
+  if constexpr (BM == 0) return c > 0 && (split == 0 || c <= split) ? 1 : 0;
+  else return split > 0 && c <= split ? 0 : (c + BM - 1) / BM;
 }
 
 template <int BM>
-__device__ __forceinline__ void find_unit(const int32_t* __restrict__ off, int E, int u, int& e_out, int& loc_out) {
+__device__ __forceinline__ void find_unit(const int32_t* __restrict__ off, int E, int split, int u, int& e_out,
+                                          int& loc_out) {
   const int lane = threadIdx.x & 63;
   const int C = (E + 63) >> 6;
   const int first = lane * C;
@@ -57,7 +62,7 @@ __device__ __forceinline__ void find_unit(const int32_t* __restrict__ off, int E
     const int e = first + i;
     if (e < E) {
       const int c = off[e + 1] - off[e];
-      units += units_of<BM>(c);
+      units += units_of<BM>(c, split);
     }
   }
   int incl = units;
@@ -82,7 +87,7 @@ __device__ __forceinline__ void find_unit(const int32_t* __restrict__ off, int E
       const int e = first + i;
       if (e < E) {
         const int c = off[e + 1] - off[e];
-        const int n = units_of<BM>(c);
+        const int n = units_of<BM>(c, split);
         if (u < acc + n) {
           ee = e;
           loc = u - acc;
@@ -118,15 +123,15 @@ __device__ __forceinline__ uint32_t lane_xor32(uint32_t x) {
 // contiguous ranges, one per XCD (block b runs on XCD b % 8). Called by a whole
 // wave; the results are wave-uniform. e_out < 0: no item for this block.
 template <int BM>
-__device__ __forceinline__ void grouped_work_item(const int32_t* __restrict__ off, int E, int ntiles, int x, int j,
-                                                  int& e_out, int& n_out, int& loc_out) {
+__device__ __forceinline__ void grouped_work_item(const int32_t* __restrict__ off, int E, int split, int ntiles, int x,
+                                                  int j, int& e_out, int& n_out, int& loc_out) {
   const int lane = threadIdx.x & 63;
   const int C = (E + 63) >> 6;
   const int first = lane * C;
   int units = 0;
   for (int i = 0; i < C; ++i) {
     const int e = first + i;
-    if (e < E) units += units_of<BM>(off[e + 1] - off[e]);
+    if (e < E) units += units_of<BM>(off[e + 1] - off[e], split);
   }
   int incl = units;
 #pragma unroll
@@ -151,7 +156,7 @@ __device__ __forceinline__ void grouped_work_item(const int32_t* __restrict__ of
     for (int i = 0; i < C; ++i) {
       const int e = first + i;
       if (e < E) {
-        const int n = units_of<BM>(off[e + 1] - off[e]);
+        const int n = units_of<BM>(off[e + 1] - off[e], split);
         if (p < acc + n) {
           ee = e;
           ue = acc;

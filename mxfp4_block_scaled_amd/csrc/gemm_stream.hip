@@ -97,7 +97,7 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
     m = (int)a.M;
   } else {
     int loc;
-    find_unit<0>(a.offsets, a.E, blockIdx.y, e, loc);
+    find_unit<0>(a.offsets, a.E, a.split, blockIdx.y, e, loc);
     if (e < 0) return;
     row0 = a.offsets[e];
     m = a.offsets[e + 1] - (int)row0;

@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(256) gemm_tile4_kernel(GemmArgs a) {
     m = (int)(a.M - row0 < BM ? a.M - row0 : BM);
   } else {
     int loc;
-    grouped_work_item<BM>(a.offsets, a.E, ntiles, x, jb, e, n_tile, loc);
+    grouped_work_item<BM>(a.offsets, a.E, a.split, ntiles, x, jb, e, n_tile, loc);
     if (e < 0) return;
     row0 = a.offsets[e] + (int64_t)loc * BM;
     m = min(BM, a.offsets[e + 1] - (int)row0);

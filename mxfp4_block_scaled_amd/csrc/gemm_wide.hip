@@ -216,14 +216,14 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
       m = (int)(a.M - row0 < BM ? a.M - row0 : BM);
     } else {
       int loc;
-      find_unit<BM>(a.offsets, a.E, m_unit, e, loc);
+      find_unit<BM>(a.offsets, a.E, 0, m_unit, e, loc);
       if (e < 0) return;
       row0 = a.offsets[e] + (int64_t)loc * BM;
       m = min(BM, a.offsets[e + 1] - (int)row0);
     }
   } else {
     int loc, n_grp;
-    grouped_work_item<BM>(a.offsets, a.E, ntiles / ntg, x, jb, e, n_grp, loc);
+    grouped_work_item<BM>(a.offsets, a.E, a.split, ntiles / ntg, x, jb, e, n_grp, loc);
     if (e < 0) return;
     n_tile = n_grp * ntg;
     row0 = a.offsets[e] + (int64_t)loc * BM;

@@ -87,6 +87,40 @@ def test_layer_skewed_routing_one_expert_takes_all():
     _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e4m3")
 
 
+@pytest.mark.parametrize("fmt,y_dtype", [("e4m3", torch.bfloat16), ("e2m1", torch.bfloat16),
+                                         ("e4m3", torch.float32)])
+def test_layer_split_small_experts_stream(fmt, y_dtype):
+    """Past 64 tokens with fewer than 64 rows per expert, experts of at most 16 rows
+    run in the streaming kernel and the others in the tiled kernels: expert loads of
+    16 | 17 | 1 | 0 | 2 x 128 + 5 | 40 | 16 | 15 rows straddle both boundaries."""
+    counts = [16, 17, 1, 0, 261, 40, 16, 15]
+    T, H, I, E, k = sum(counts), 1024, 512, len(counts), 1
+    x = dg.activations(15, T, H)
+    logits = dg.logits(15, T, E, "normal")
+    owner = np.repeat(np.arange(E), counts)
+    np.random.default_rng(15).shuffle(owner)
+    logits[np.arange(T), owner] += 50.0
+    w1, s1, w2, s2 = dg.moe_weights(15, E, H, I, 120, 128)
+    g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, fmt, y_dtype=y_dtype)
+    assert np.array_equal(np.diff(g["expert_offsets"]), counts)
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, fmt)
+    _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_layer_split_zipf_routing(fmt):
+    # skewed routing over 64 experts: a few hot experts in tiles, a long tail streamed
+    T, H, I, E, k = 240, 1024, 1024, 64, 2
+    x = dg.activations(16, T, H)
+    logits = dg.logits(16, T, E, "zipf")
+    w1, s1, w2, s2 = dg.moe_weights(16, E, H, I, 120, 128)
+    g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, fmt)
+    c = np.diff(g["expert_offsets"])
+    assert (c > 16).any() and ((c > 0) & (c <= 16)).any()
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, fmt)
+    _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt)
+
+
 @pytest.mark.parametrize("T", [24, 10])  # two 16-row fragments / one (FC2 with two row blocks)
 def test_layer_fp32_y(T):
     H, I, E, k = 512, 512, 8, 3
