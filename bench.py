@@ -43,7 +43,7 @@ BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,
 # passes, scaled by a 1 GiB copy (2.0 x FETCH_SIZE + 1.0 x WRITE_SIZE; the passes and the
 # calibration are in profiles/moe_layer_hbm_traffic.md). They hold only for the GEMM sources
 # they were measured on (sha-256 over GEMM_SOURCES): on any other source traffic = null.
-TRAFFIC_SRC_SHA256 = "b02d4571c69b9c44676591f29c524ec621c5e9f9ab500ca4d15e90c500ae519a"
+TRAFFIC_SRC_SHA256 = "d1136d728a94c1ff832ba1fb8b3ab2b52fd2df32fe3da2d2b0a0a81969af76db"
 TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8715523936, "moe_decode_t8": 1008555744}
 
 

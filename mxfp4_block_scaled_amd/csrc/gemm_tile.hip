@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(256) gemm_tile4_kernel(GemmArgs a) {
   // fixed; the stage advances a scalar offset.
   const buf_rsrc ra = make_rsrc(a.act, (uint32_t)(a.act_rows * arow));
   const buf_rsrc ras = make_rsrc(a.act_scale, (uint32_t)(a.act_rows * srow));
-  // e is the same in every lane (find_unit broadcasts it); say so, so that the
+  // e is the same in every lane (the work-item lookup broadcasts it); say so, so that the
   // weight resources live in scalar registers
   const int eu = __builtin_amdgcn_readfirstlane(e);
   const buf_rsrc rb = make_rsrc(a.w + (int64_t)eu * a.N * wrow, (uint32_t)(a.N * wrow));
