@@ -1,0 +1,85 @@
+"""HIP graph capture of the C-ABI calls: the library allocates, frees, clears and
+synchronises nothing, so a whole layer step (or a dense GEMM with its workspace)
+can be captured once and replayed. Every replay must reproduce the eager result
+bit for bit (the kernels are deterministic), also after the static inputs have
+been overwritten and with eager work and synchronisations between replays."""
+
+import numpy as np
+import pytest
+import torch
+
+from mxfp4_block_scaled_amd import datagen as dg
+from mxfp4_block_scaled_amd import ops
+from tests.helpers import bf16_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _capture(fn):
+    # warm up on a side stream (first calls load the library), then capture
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = fn()
+    return g, out
+
+
+def _assert_same(got, want):
+    for key in want:
+        assert torch.equal(got[key], want[key]), key
+
+
+@pytest.mark.parametrize("T,H,I,E,k,fmt", [
+    (8, 1024, 512, 16, 6, "e4m3"),    # decode: streaming kernels
+    (300, 1024, 512, 8, 6, "e4m3"),   # FP8 tiles
+    (300, 1024, 1024, 8, 4, "e2m1"),  # FP4 256 x 256 tiles
+    (240, 1024, 1024, 64, 2, "e2m1"), # few rows per expert: streamed small experts + tiles
+])
+def test_layer_graph_replays_match_eager(T, H, I, E, k, fmt):
+    w = [torch.from_numpy(np.ascontiguousarray(t)).cuda() for t in dg.moe_weights(31, E, H, I, 120, 128)]
+    routing = "zipf" if E == 64 else "normal"
+    xa, xb = bf16_dev(dg.activations(31, T, H)), bf16_dev(dg.activations(32, T, H))
+    la = torch.from_numpy(dg.logits(31, T, E, routing)).cuda()
+    lb = torch.from_numpy(dg.logits(32, T, E, routing)).cuda()
+    x, logits = xa.clone(), la.clone()  # the graph's static inputs
+
+    def step():
+        return ops.moe_layer(x, logits, *w, topk=k, act_fmt=fmt)
+
+    want_a = {key: v.clone() for key, v in ops.moe_layer(xa, la, *w, topk=k, act_fmt=fmt).items()}
+    want_b = {key: v.clone() for key, v in ops.moe_layer(xb, lb, *w, topk=k, act_fmt=fmt).items()}
+    g, out = _capture(step)
+    for rep, (xi, li, want) in enumerate([(xa, la, want_a), (xb, lb, want_b), (xa, la, want_a)]):
+        x.copy_(xi)
+        logits.copy_(li)
+        ops.moe_layer(xb if rep % 2 == 0 else xa, lb if rep % 2 == 0 else la, *w, topk=k, act_fmt=fmt)  # eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _assert_same(out, want)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 32, 4096), (64, 512, 7168), (100, 256, 1024)])
+def test_dense_graph_replays_match_eager(M, N, K):
+    a0, ww, ss = (dg.activations(33, M, K),) + tuple(dg.dense_weights(33, N, K, 122, 130))
+    w, s = torch.from_numpy(ww).cuda(), torch.from_numpy(ss).cuda()
+    aa, ab = bf16_dev(a0), bf16_dev(dg.activations(34, M, K))
+    a = aa.clone()
+    need = ops.load().mxfp4_gemm_workspace_bytes(M, N, K, ops.FMTS["e4m3"])
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    want_a = ops.mxfp4_gemm(aa, w, s).clone()
+    want_b = ops.mxfp4_gemm(ab, w, s).clone()
+    g, _ = _capture(lambda: ops.mxfp4_gemm(a, w, s, out=c, workspace=ws))
+    for rep, (ai, want) in enumerate([(aa, want_a), (ab, want_b), (aa, want_a)]):
+        a.copy_(ai)
+        ops.mxfp4_gemm(ab if rep % 2 == 0 else aa, w, s)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c, want), rep
