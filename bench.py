@@ -233,8 +233,28 @@ def bench_dense(steps, warmup, rotate=48):
 
     wall, st = time_steps(step, steps * 10, warmup, nev=2)
     ms = float(np.mean(st[:, 0]))
+    # the same calls back to back from one HIP graph (one call per weight set)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(None)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(len(sets)):
+            step(None)
+    for _ in range(max(warmup, 1)):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(steps // 4, 2)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) / (reps * len(sets)) * 1e3
     wbytes = N * K // 2 + N * K // 32
-    return dict(ms=ms, wbytes=wbytes, gbs=wbytes / (ms * 1e-3) / 1e9, flops=2 * M * N * K)
+    return dict(ms=ms, graph_ms=graph_ms, wbytes=wbytes, gbs=wbytes / (ms * 1e-3) / 1e9, flops=2 * M * N * K)
 
 
 def cpu_baseline(name, budget_s=15.0):
@@ -349,7 +369,9 @@ def main():
         r = bench_dense(args.steps, args.warmup)
         result["dense"] = {"workload": "dense_m64_n4096_k7168", "ms": round(r["ms"], 5),
                            "weight_GBps": round(r["gbs"], 1), "frac_hbm": round(r["gbs"] / PEAK_HBM_GBS, 4),
-                           "TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2)}
+                           "TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
+                           "graph": {"ms": round(r["graph_ms"], 5),
+                                     "weight_GBps": round(r["wbytes"] / (r["graph_ms"] * 1e-3) / 1e9, 1)}}
     if not args.no_cpu and args.only in (None, "prefill"):
         log("[bench] timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline("moe_prefill_t16384_fp4")
