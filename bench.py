@@ -300,7 +300,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "dense", "copy"], default=None)
+    # "skewed": the 2048-token Zipf-routed FP8 layer, only when asked for (not in the default line)
+    ap.add_argument("--only", choices=["prefill", "decode", "dense", "skewed", "copy"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the expert path here is the "
@@ -363,6 +364,17 @@ def main():
                            "dtype": "mxfp8 x mxfp4 (e4m3 x e2m1, fp32 accumulate)",
                            "config": {"workload": name}, "roofline": dec["roofline"]})
         result["decode"] = dec
+        del r["layer"]
+        torch.cuda.empty_cache()
+    if args.only == "skewed":
+        name = "moe_prefill_t2048_zipf"
+        r = bench_moe(name, args.steps, args.warmup, rotate=1)
+        g_ms = r["stage_ms"]["grouped_gemm"]
+        result["skewed"] = {"workload": name, "ms_per_step": round(r["ms"], 4),
+                            "stages_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
+                            "touched_experts": r["touched"], "max_rows_per_expert": r["max_rows"],
+                            "grouped_TFLOPs": round(r["flops"] / (g_ms * 1e-3) / 1e12, 1),
+                            "touched_weight_GBps_grouped": round(r["wbytes"] / (g_ms * 1e-3) / 1e9, 1)}
         del r["layer"]
         torch.cuda.empty_cache()
     if args.only in (None, "dense"):
