@@ -257,6 +257,45 @@ def bench_dense(steps, warmup, rotate=48):
     return dict(ms=ms, graph_ms=graph_ms, wbytes=wbytes, gbs=wbytes / (ms * 1e-3) / 1e9, flops=2 * M * N * K)
 
 
+def measure_ceilings(reps=3):
+    """What this GPU sustains for the two bounds (include/mxf_ceilings.h), best of
+    `reps`: a non-temporal streaming read of 2 GiB, and register-only loops of
+    32x32x64 scaled MFMAs on random operand bits (E2M1 x E2M1, E4M3 x E2M1)."""
+    lib = ops.load()
+    st = ctypes_stream()
+    buf = torch.ones(1 << 29, dtype=torch.int32, device="cuda")  # 2 GiB
+    xo = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(17)
+    words = torch.randint(-2**31, 2**31 - 1, (ops.CEILING_MFMA_WORDS,), dtype=torch.int32, device="cuda",
+                          generator=g)
+    sink = torch.empty(ops.CEILING_MFMA_GROUPS, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn):
+        fn()
+        t = []
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return min(t)
+
+    nbytes = buf.numel() * 4
+    ms_read = best(lambda: ops._check(lib.mxf_ceiling_read(ops._ptr(buf), nbytes, ops._ptr(xo), st), "read"))
+    iters = 20000
+    flops = lib.mxf_ceiling_mfma_flops(iters)
+    out = {"hbm_read_GBps": round(nbytes / (ms_read * 1e-3) / 1e9, 1)}
+    for key, f in (("mfma_e2m1_random_TFLOPs", ops.MXF_E2M1), ("mfma_e4m3xe2m1_random_TFLOPs", ops.MXF_E4M3)):
+        ms = best(lambda: ops._check(lib.mxf_ceiling_mfma(f, ops._ptr(words), words.numel(), 124, iters,
+                                                          ops._ptr(sink), st), "mfma"))
+        out[key] = round(flops / (ms * 1e-3) / 1e12, 1)
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(name, budget_s=15.0):
     """The fp64 oracle (as it stands) on a bounded sample: whole experts of the
     headline layer, all their rows, until ~budget_s of CPU time is spent."""
@@ -322,6 +361,8 @@ def main():
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
 
+    ceil = measure_ceilings()
+    result["ceilings"] = ceil
     if args.only in (None, "prefill"):
         name = "moe_prefill_t16384_fp4"
         r = bench_moe(name, args.steps, args.warmup, rotate=1)
@@ -340,6 +381,7 @@ def main():
             "roofline": {"kernel": "moe_grouped_mxfp4_gemm (FC1 + FC2 kernels)", "bound": "mfma",
                          "achieved": round(g_tflops, 3), "peak": peak, "unit": "TFLOP/s",
                          "frac": round(g_tflops / peak, 4), "traffic": measured_traffic(name)},
+            "frac_of_measured_ceiling": round(g_tflops / ceil["mfma_e2m1_random_TFLOPs"], 4),
         })
         del r["layer"]
         torch.cuda.empty_cache()
@@ -357,6 +399,7 @@ def main():
                             "unit": "GB/s", "frac": round(r["wbytes"] / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                             "traffic": measured_traffic(name)}}
         g_wall = time_graph_steps(r["layer"], args.steps * 5, args.warmup)
+        dec["frac_of_measured_ceiling"] = round(dec["roofline"]["achieved"] / ceil["hbm_read_GBps"], 4)
         dec["graph"] = {"ms_per_step": round(g_wall * 1e3, 4),
                         "weight_GBps_layer": round(r["wbytes"] / g_wall / 1e9, 1)}
         if "value" not in result:
@@ -375,6 +418,12 @@ def main():
                             "touched_experts": r["touched"], "max_rows_per_expert": r["max_rows"],
                             "grouped_TFLOPs": round(r["flops"] / (g_ms * 1e-3) / 1e12, 1),
                             "touched_weight_GBps_grouped": round(r["wbytes"] / (g_ms * 1e-3) / 1e9, 1)}
+        sk = result["skewed"]
+        sk["frac_fp8_peak"] = round(sk["grouped_TFLOPs"] / PEAK_TFLOPS["e4m3"], 4)
+        sk["frac_hbm_peak"] = round(sk["touched_weight_GBps_grouped"] / PEAK_HBM_GBS, 4)
+        sk["frac_of_measured_ceilings"] = {
+            "mfma": round(sk["grouped_TFLOPs"] / ceil["mfma_e4m3xe2m1_random_TFLOPs"], 4),
+            "hbm": round(sk["touched_weight_GBps_grouped"] / ceil["hbm_read_GBps"], 4)}
         del r["layer"]
         torch.cuda.empty_cache()
     if args.only in (None, "dense"):

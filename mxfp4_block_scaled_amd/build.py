@@ -31,7 +31,7 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-function",
 ]
-SOURCES = ["quantize.hip", "route.hip", "gemm.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "combine.hip", "abi.cpp"]
+SOURCES = ["quantize.hip", "route.hip", "gemm.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "combine.hip", "ceilings.hip", "abi.cpp"]
 
 
 def _compile(src, verbose):

@@ -31,7 +31,14 @@ SIGNATURES = {
     "moe_grouped_mxfp4_gemm": (_c_int, [_p, _p, _c_int, _c_i64, _c_i32, _c_i64, _c_i64, _c_i32,
                                         _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_int, _p]),
     "moe_unpermute_combine": (_c_int, [_p, _c_int, _p, _p, _c_i64, _c_i32, _c_i64, _p, _c_int, _p]),
+    # include/mxf_ceilings.h: achievable-rate probes (measurement helpers)
+    "mxf_ceiling_mfma_flops": (_c_i64, [_c_int]),
+    "mxf_ceiling_mfma": (_c_int, [_c_int, _p, _c_i64, _c_int, _c_int, _p, _p]),
+    "mxf_ceiling_read": (_c_int, [_p, _c_i64, _p, _p]),
 }
+
+CEILING_MFMA_GROUPS = 512
+CEILING_MFMA_WORDS = 64 * 6 * 64 * 8
 
 
 def lib_path():
@@ -162,3 +169,28 @@ def moe_layer(x, logits, w1, w1_scale, w2, w2_scale, topk, act_fmt="e4m3", y_dty
     out = moe_unpermute_combine(y, gates, pr, T, topk, out_dtype)
     return dict(q=q, q_scale=qs, topk_ids=ids, gates=gates, expert_offsets=offs, sorted_pair=sp, pair_row=pr,
                 h=h, h_scale=hs, y=y, out=out)
+
+
+def ceiling_mfma(operands, act_fmt="e2m1", scale=127, iters=2000, sink=None):
+    """Register-only scaled-MFMA loop (include/mxf_ceilings.h); returns (sink, flops).
+    operands: int32 device tensor of >= CEILING_MFMA_WORDS words."""
+    dev = _dev(operands)
+    if operands.dtype != torch.int32:
+        raise RuntimeError("operands must be int32")
+    if sink is None:
+        sink = torch.empty(CEILING_MFMA_GROUPS, dtype=torch.float32, device=dev)
+    lib = load()
+    _check(lib.mxf_ceiling_mfma(FMTS[act_fmt], _ptr(operands), operands.numel(), scale, iters, _ptr(sink),
+                                _stream(dev)), "mxf_ceiling_mfma")
+    return sink, lib.mxf_ceiling_mfma_flops(iters)
+
+
+def ceiling_read(buf, xor_out=None):
+    """Streaming non-temporal read of a device buffer; returns the int32 tensor holding
+    the XOR of all its 32-bit words (accumulated into xor_out when given)."""
+    dev = _dev(buf)
+    if xor_out is None:
+        xor_out = torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = buf.numel() * buf.element_size()
+    _check(load().mxf_ceiling_read(_ptr(buf), nbytes, _ptr(xor_out), _stream(dev)), "mxf_ceiling_read")
+    return xor_out

@@ -23,9 +23,14 @@ def _lib():
     return ops.load()
 
 
-def _declared():
-    text = open(HEADER).read()
-    return re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+def _declared(headers=(HEADER,)):
+    text = "".join(open(h).read() for h in headers)
+    return re.findall(r"^\s*(?:int|int64_t|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def _all_headers():
+    inc = os.path.join(ROOT, "include")
+    return [os.path.join(inc, f) for f in sorted(os.listdir(inc)) if f.endswith(".h")]
 
 
 def test_header_declares_the_five_entry_points():
@@ -37,7 +42,9 @@ def test_header_declares_the_five_entry_points():
 
 def test_library_exports_every_declared_symbol():
     lib = _lib()
-    for name in _declared():
+    names = _declared(_all_headers())
+    assert "mxf_ceiling_mfma" in names and "mxf_ceiling_read" in names
+    for name in names:
         assert hasattr(lib, name), name
     assert lib.mxf_abi_version() == 2
     for s in range(8):
@@ -134,3 +141,20 @@ def test_combine_errors():
     assert lib.moe_unpermute_combine(A, 1, None, A, 8, 6, 7168, A, 1, None) == NULL
     assert lib.moe_unpermute_combine(A, 1, A, A, 8, 6, 7168, U, 1, None) == ALIGN
     assert lib.moe_unpermute_combine(None, 1, None, None, 0, 6, 7168, None, 1, None) == OK
+
+
+def test_ceiling_probe_errors():
+    lib = _lib()
+    W = ops.CEILING_MFMA_WORDS
+    assert lib.mxf_ceiling_mfma_flops(10) == 512 * 4 * 10 * 8 * 131072
+    assert lib.mxf_ceiling_mfma_flops(0) == 0
+    assert lib.mxf_ceiling_mfma(2, A, W, 127, 10, A, None) == FORMAT
+    assert lib.mxf_ceiling_mfma(1, A, W - 1, 127, 10, A, None) == SHAPE
+    assert lib.mxf_ceiling_mfma(1, A, W, 127, 0, A, None) == SHAPE
+    assert lib.mxf_ceiling_mfma(1, A, W, 255, 10, A, None) == SHAPE
+    assert lib.mxf_ceiling_mfma(1, None, W, 127, 10, A, None) == NULL
+    assert lib.mxf_ceiling_mfma(1, U, W, 127, 10, A, None) == ALIGN
+    assert lib.mxf_ceiling_read(A, 40, A, None) == SHAPE
+    assert lib.mxf_ceiling_read(None, 64, A, None) == NULL
+    assert lib.mxf_ceiling_read(U, 64, A, None) == ALIGN
+    assert lib.mxf_ceiling_read(None, 0, None, None) == OK
