@@ -176,6 +176,27 @@ def test_layer_workloads(name, ntok):
     _compare(g, ref, d["x"], d["logits"], *w, k, fmt, rows=rows, tokens=tokens)
 
 
+def test_skewed_workload_streamed_and_tiled_experts():
+    """The full-size Zipf-routed layer runs its experts of at most 16 rows in the
+    streaming kernels and the others in tiles: sample tokens with pairs in both."""
+    name = "moe_prefill_t2048_zipf"
+    d = dg.workload_inputs(name)
+    cfg = d["cfg"]
+    k, fmt, T = cfg["k"], cfg["act_fmt"], cfg["T"]
+    w = (d["w1"], d["s1"], d["w2"], d["s2"])
+    g = _layer(d["x"], d["logits"], _dev_weights(*w), k, fmt)
+    counts = np.diff(g["expert_offsets"])
+    ids = g["topk_ids"].reshape(T, k)
+    small = (counts > 0) & (counts <= 16)
+    assert small.any() and (counts > 16).any()
+    has_small = np.nonzero(small[ids].any(axis=1))[0]
+    all_large = np.nonzero(~small[ids].any(axis=1))[0]
+    tokens = [int(t) for t in has_small[:4]] + [int(t) for t in all_large[:2]]
+    rows = [int(g["pair_row"][t * k + j]) for t in tokens for j in range(k)]
+    ref = oracle.moe_layer(d["x"], d["logits"], *w, k, fmt, rows=rows)
+    _compare(g, ref, d["x"], d["logits"], *w, k, fmt, rows=rows, tokens=tokens)
+
+
 def test_layer_is_deterministic():
     T, H, I, E, k = 300, 1024, 512, 8, 6
     x = bf16_dev(dg.activations(21, T, H))
