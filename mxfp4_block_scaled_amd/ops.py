@@ -83,10 +83,28 @@ def _dev(t):
     return t.device
 
 
+def _need(t, name, dtypes, shape):
+    """Raise unless t has one of `dtypes` and the given shape; a shape entry given
+    as (">=", n) only bounds that dimension from below."""
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise RuntimeError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if t.dim() != len(shape):
+        raise RuntimeError(f"{name}: {t.dim()}-d, expected {len(shape)}-d {shape}")
+    for i, (got, want) in enumerate(zip(t.shape, shape)):
+        ok = got >= want[1] if isinstance(want, tuple) else got == want
+        if not ok:
+            raise RuntimeError(f"{name}: shape {tuple(t.shape)}, expected {shape} (dimension {i})")
+
+
 def mxfp4_quantize_act(x, fmt="e4m3"):
     """x [rows][K] bf16/fp32 -> (q [rows][K] or [rows][K/2] uint8, q_scale [rows][K/32] uint8)."""
     dev = _dev(x)
+    if x.dim() != 2:
+        raise RuntimeError("x must be 2-d [rows][K]")
     rows, K = x.shape
+    _need(x, "x", (torch.bfloat16, torch.float32), (rows, K))
     f = FMTS[fmt]
     q = torch.empty((rows, K // 2 if f == MXF_E2M1 else K), dtype=torch.uint8, device=dev)
     qs = torch.empty((rows, K // 32), dtype=torch.uint8, device=dev)
@@ -99,14 +117,23 @@ def mxfp4_gemm(a, w, w_scale, act_fmt="e4m3", out=None, workspace=None):
     """a [M][K] bf16, w [N][K/2] uint8, w_scale [N][K/32] uint8 -> c [M][N] fp32."""
     dev = _dev(a)
     _dev(w), _dev(w_scale)
+    if a.dim() != 2 or w.dim() != 2:
+        raise RuntimeError("a must be [M][K] and w [N][K/2]")
     M, K = a.shape
     N = w.shape[0]
+    _need(a, "a", torch.bfloat16, (M, K))
+    _need(w, "w", torch.uint8, (N, K // 2))
+    _need(w_scale, "w_scale", torch.uint8, (N, K // 32))
     f = FMTS[act_fmt]
     lib = load()
     need = lib.mxfp4_gemm_workspace_bytes(M, N, K, f)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace)
+    _need(workspace, "workspace", torch.uint8, ((">=", need),))
     c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    _dev(c)
+    _need(c, "out", torch.float32, (M, N))
     _check(lib.mxfp4_gemm(_ptr(a), M, N, K, f, _ptr(w), _ptr(w_scale), _ptr(c), _ptr(workspace),
                           workspace.numel(), _stream(dev)), "mxfp4_gemm")
     return c
@@ -115,7 +142,10 @@ def mxfp4_gemm(a, w, w_scale, act_fmt="e4m3", out=None, workspace=None):
 def moe_route_permute(logits, topk):
     """logits [T][E] fp32 -> (topk_ids, gates, expert_offsets, sorted_pair, pair_row)."""
     dev = _dev(logits)
+    if logits.dim() != 2:
+        raise RuntimeError("logits must be [T][E]")
     T, E = logits.shape
+    _need(logits, "logits", torch.float32, (T, E))
     ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
     gates = torch.empty((T, topk), dtype=torch.float32, device=dev)
     offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
@@ -130,17 +160,35 @@ def moe_grouped_mxfp4_gemm(q, q_scale, act_fmt, T, topk, expert_offsets, sorted_
                            w2_scale, y_dtype=torch.bfloat16, h=None, h_scale=None, y=None):
     """Both expert FCs. Returns (h, h_scale, y) with y [T*topk][H] in permuted row order."""
     dev = _dev(q)
+    for t in (q_scale, expert_offsets, sorted_pair, w1, w1_scale, w2, w2_scale):
+        _dev(t)
+    if w1.dim() != 3:
+        raise RuntimeError("w1 must be [E][2I][H/2]")
     E, twoI, Hh = w1.shape
     I = twoI // 2
     H = Hh * 2
     f = FMTS[act_fmt]
     R = T * topk
+    fp4 = f == MXF_E2M1
+    _need(q, "q", torch.uint8, (T, H // 2 if fp4 else H))
+    _need(q_scale, "q_scale", torch.uint8, (T, H // 32))
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    _need(sorted_pair, "sorted_pair", torch.int32, ((">=", R),))
+    _need(w1, "w1", torch.uint8, (E, 2 * I, H // 2))
+    _need(w1_scale, "w1_scale", torch.uint8, (E, 2 * I, H // 32))
+    _need(w2, "w2", torch.uint8, (E, H, I // 2))
+    _need(w2_scale, "w2_scale", torch.uint8, (E, H, I // 32))
     if h is None:
-        h = torch.empty((max(R, 1), I // 2 if f == MXF_E2M1 else I), dtype=torch.uint8, device=dev)
+        h = torch.empty((max(R, 1), I // 2 if fp4 else I), dtype=torch.uint8, device=dev)
     if h_scale is None:
         h_scale = torch.empty((max(R, 1), I // 32), dtype=torch.uint8, device=dev)
     if y is None:
         y = torch.empty((max(R, 1), H), dtype=y_dtype, device=dev)
+    for t in (h, h_scale, y):
+        _dev(t)
+    _need(h, "h", torch.uint8, ((">=", R), I // 2 if fp4 else I))
+    _need(h_scale, "h_scale", torch.uint8, ((">=", R), I // 32))
+    _need(y, "y", (torch.float32, torch.bfloat16), ((">=", R), H))
     _check(load().moe_grouped_mxfp4_gemm(
         _ptr(q), _ptr(q_scale), f, T, topk, H, I, E, _ptr(expert_offsets), _ptr(sorted_pair), _ptr(w1),
         _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(h), _ptr(h_scale), _ptr(y), DTYPES[y.dtype],
@@ -151,9 +199,17 @@ def moe_grouped_mxfp4_gemm(q, q_scale, act_fmt, T, topk, expert_offsets, sorted_
 def moe_unpermute_combine(y, gates, pair_row, T, topk, out_dtype=torch.bfloat16, out=None):
     """out [T][H] = sum_j gates[t, j] * y[pair_row[t*topk + j]]."""
     dev = _dev(y)
+    _dev(gates), _dev(pair_row)
+    if y.dim() != 2:
+        raise RuntimeError("y must be [T*topk][H]")
     H = y.shape[1]
+    _need(y, "y", (torch.float32, torch.bfloat16), ((">=", T * topk), H))
+    _need(gates, "gates", torch.float32, (T, topk))
+    _need(pair_row, "pair_row", torch.int32, ((">=", T * topk),))
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    _dev(out)
+    _need(out, "out", (torch.float32, torch.bfloat16), (T, H))
     _check(load().moe_unpermute_combine(_ptr(y), DTYPES[y.dtype], _ptr(gates), _ptr(pair_row), T, topk, H,
                                         _ptr(out), DTYPES[out.dtype], _stream(dev)), "moe_unpermute_combine")
     return out

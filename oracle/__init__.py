@@ -53,6 +53,7 @@ from .moe import (  # noqa: F401
     swiglu,
     moe_layer,
     fc1_swiglu_rows,
+    fc1_abs_terms,
     fc2_rows,
     combine,
     row_normalised_error,

@@ -121,7 +121,14 @@ def combine(y, gates, pair_row, T, k):
     return out
 
 
-def moe_layer(x_bf16, logits, w1, s1, w2, s2, k, act_fmt, rows=None):
+def fc1_abs_terms(a_hat_rows, w1, w1_scale):
+    """S[r, n] = sum_k |a_hat[r, k]| * |W1_hat[n, k]|: the sum of the magnitudes of
+    the products that FC1 adds up (not part of the layer's result; it scales the
+    rounding error of any finite-precision summation of those products)."""
+    return np.abs(a_hat_rows) @ np.abs(dequant_weights(w1, w1_scale)).T
+
+
+def moe_layer(x_bf16, logits, w1, s1, w2, s2, k, act_fmt, rows=None, workers=1, abs_terms=False):
     """The whole expert layer, expert by expert, in fp64.
 
     x_bf16 [T][H] bf16 bits; logits [T][E] fp32; w1 [E][2I][H/2], s1 [E][2I][H/32],
@@ -130,6 +137,9 @@ def moe_layer(x_bf16, logits, w1, s1, w2, s2, k, act_fmt, rows=None):
     None computes every row. Returns a dict of every intermediate; y / h / G
     entries are only filled for the computed rows, and 'out' only for tokens
     all of whose k rows were computed (others are NaN).
+    workers: experts are independent; with workers > 1 they are computed on that
+    many threads (the same per-expert arithmetic, only run concurrently).
+    abs_terms: also return 'G_abs' = fc1_abs_terms of the computed rows.
     """
     x_bf16 = np.asarray(x_bf16)
     T, H = x_bf16.shape
@@ -149,18 +159,30 @@ def moe_layer(x_bf16, logits, w1, s1, w2, s2, k, act_fmt, rows=None):
     h_codes = np.zeros((R, I // 2 if act_fmt == FMT_E2M1 else I), dtype=np.uint8)
     h_scale = np.zeros((R, I // 32), dtype=np.uint8)
     y = np.full((R, H), np.nan)
-    for e in range(E):
+    G_abs = np.full((R, 2 * I), np.nan) if abs_terms else None
+
+    def one_expert(e):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         r = np.arange(lo, hi)
         r = r[want[lo:hi]]
         if r.size == 0:
-            continue
+            return
         tok = sorted_pair[r] // k
         a_hat = decode_act(q[tok], q_scale[tok], act_fmt)
         Ge, he = fc1_swiglu_rows(a_hat, w1[e], s1[e], I)
         hq, hs = quantize_act(he, act_fmt)
         G[r], h_pre[r], h_codes[r], h_scale[r] = Ge, he, hq, hs
         y[r] = fc2_rows(hq, hs, act_fmt, w2[e], s2[e])
+        if abs_terms:
+            G_abs[r] = fc1_abs_terms(a_hat, w1[e], s1[e])
+
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one_expert, range(E)))
+    else:
+        for e in range(E):
+            one_expert(e)
     out = np.full((T, H), np.nan)
     done = want[pair_row.reshape(T, k)].all(axis=1)
     if done.any():
@@ -172,7 +194,7 @@ def moe_layer(x_bf16, logits, w1, s1, w2, s2, k, act_fmt, rows=None):
         out[tk] = acc
     return dict(q=q, q_scale=q_scale, topk_ids=topk_ids, gates=gates,
                 expert_offsets=offsets, sorted_pair=sorted_pair, pair_row=pair_row,
-                G=G, h_pre=h_pre, h=h_codes, h_scale=h_scale, y=y, out=out,
+                G=G, G_abs=G_abs, h_pre=h_pre, h=h_codes, h_scale=h_scale, y=y, out=out,
                 computed_rows=want, computed_tokens=done)
 
 

@@ -72,3 +72,81 @@ def straddle_check(gpu_codes, gpu_scale, h_pre, fmt, tol=1e-3):
 
 def unpack_codes(h, fmt):
     return oracle.unpack_e2m1(h) if fmt == "e2m1" else h
+
+
+# FC1 accumulation error of the scaled matrix instructions, per output element:
+# |G_gpu - G_exact| <= MFMA_RESIDUAL * sum_k |a_k w_k|. Measured by
+# tests/test_gpu_mfma_residual.py at K = 7168 (both activation formats, both
+# instruction shapes); the constant there is the one used here.
+MFMA_RESIDUAL = {"e4m3": 2.0 ** -13, "e2m1": 2.0 ** -17}
+# relative error of the fp32 SwiGLU (hardware exp and reciprocal, a few ulp each)
+SWIGLU_REL = 2.0 ** -19
+SILU_SLOPE_MAX = 1.1  # sup |d silu / dx| = 1.0998...
+
+
+def h_error_bound(G, G_abs, I, fmt):
+    """Per-element bound on |h_gpu - h_exact| for h = silu(g) * u, from the bound on
+    the FC1 accumulators: |silu(g+dg)(u+du) - silu(g) u| <= 1.1 |dg| (|u| + |du|)
+    + |silu(g)| |du|, plus the fp32 evaluation error of SwiGLU itself."""
+    g, u = G[:, :I], G[:, I:2 * I]
+    dg = MFMA_RESIDUAL[fmt] * G_abs[:, :I]
+    du = MFMA_RESIDUAL[fmt] * G_abs[:, I:2 * I]
+    silu = g / (1.0 + np.exp(-np.clip(g, -700, 700)))
+    h = silu * u
+    return SILU_SLOPE_MAX * dg * (np.abs(u) + du) + np.abs(silu) * du + SWIGLU_REL * np.abs(h)
+
+
+def straddle_check_bound(gpu_codes, gpu_scale, h_pre, dh, fmt):
+    """Requantised h judged against a per-element error bound dh (h_error_bound).
+
+    A GPU scale byte may differ from the oracle's only where the block amax lies
+    within the block's largest dh of a power of two; every GPU code (at the GPU's
+    own scale byte) must then be a correct rounding of some value within dh of the
+    oracle's exact h: the oracle value, scaled, lies within dh (scaled) of the
+    rounding interval of the GPU code (signed: +0 covers [0, first midpoint], -0 the
+    mirror image). Returns (n_code_mismatch, n_scale_mismatch)."""
+    ref_codes, ref_scale = oracle.mx_quantize(h_pre, fmt)
+    R, I = h_pre.shape
+    nb = I // 32
+    blk = h_pre.reshape(R, nb, 32)
+    dblk = dh.reshape(R, nb, 32)
+    amax = np.abs(blk).max(-1)
+    sc_bad = gpu_scale != ref_scale
+    if sc_bad.any():
+        a = amax[sc_bad]
+        p2 = np.exp2(np.round(np.log2(np.maximum(a, 1e-300))))
+        slack = dblk.max(-1)[sc_bad]
+        assert np.all(np.abs(a - p2) <= slack), \
+            f"scale byte differs away from a power-of-two amax: {a[np.abs(a - p2) > slack][:5]}"
+        assert np.all(np.abs(gpu_scale.astype(int) - ref_scale.astype(int))[sc_bad] == 1), "scale bytes 2+ apart"
+    dec = oracle.e4m3_decode if fmt == "e4m3" else oracle.e2m1_decode
+    gc = gpu_codes.reshape(R, nb, 32)
+    # the oracle's codes at the GPU's scale byte: equal to ref_codes where the bytes agree
+    xg = gpu_scale.astype(np.int64) - 127
+    t = np.ldexp(blk, -xg[..., None])
+    mag = oracle.round_to_grid(np.abs(t), fmt)
+    sign_bit = 0x80 if fmt == "e4m3" else 0x8
+    at_gpu_scale = np.where(np.signbit(blk), mag | sign_bit, mag).astype(np.uint8)
+    bad = gc != at_gpu_scale
+    n_code = int(bad.sum())
+    if n_code:
+        rr, bb, kk = np.nonzero(bad)
+        tv = t[rr, bb, kk]
+        tol = np.ldexp(dblk[rr, bb, kk], -xg[rr, bb])
+        codes = gc[rr, bb, kk]
+        gval = dec(codes)
+        assert np.all(np.isfinite(gval)), "GPU code is NaN"
+        grid = np.unique(np.abs(dec(np.arange(256 if fmt == "e4m3" else 16, dtype=np.uint8))))
+        grid = grid[np.isfinite(grid)]
+        mabs = np.abs(gval)
+        i = np.searchsorted(grid, mabs)
+        assert np.all(grid[np.minimum(i, grid.size - 1)] == mabs), "GPU code off the grid"
+        lo_b = np.where(i > 0, (grid[np.maximum(i - 1, 0)] + mabs) / 2, 0.0)
+        hi_b = np.where(i + 1 < grid.size, (mabs + grid[np.minimum(i + 1, grid.size - 1)]) / 2, np.inf)
+        neg = (codes & sign_bit) != 0
+        lo_s, hi_s = np.where(neg, -hi_b, lo_b), np.where(neg, -lo_b, hi_b)
+        dist = np.maximum(np.maximum(lo_s - tv, tv - hi_s), 0.0)
+        worst = np.argmax(dist - tol)
+        assert np.all(dist <= tol), (f"code differs beyond the error bound: t={tv[worst]} code={codes[worst]} "
+                                     f"dist={dist[worst]} tol={tol[worst]}")
+    return n_code, int(sc_bad.sum())

@@ -1,0 +1,115 @@
+"""Full-size prefill layers against the oracle on every expert.
+
+Which experts a token is routed to decides whether a kernel error shows ("【DeepSeek
+V4】Triton FP4 优化实战", "为什么中文对、英文错？" and the lessons at its end: a
+kernel can be wrong for some experts and look right for the prompts that avoid
+them). So at the 16384-token FP4 layer (uniform routing: all 256 experts, one or
+two 256-row units each) and the 2048-token Zipf-routed FP8 layer (experts of
+1..16 rows streamed, larger ones in 128-row tiles), the oracle computes the first
+and the last row of every row unit of every touched expert (every row of a
+streamed expert), and every row of the tokens that own them:
+
+* the integer outputs of the whole layer (q, q_scale, routing, permutation) are
+  bit-exact for all tokens;
+* h: the GPU's codes are correct roundings within the per-element error bound of
+  the oracle's exact h (tests/helpers.py);
+* y: stage-isolated (the oracle's FC2 on the GPU's own h), row-normalised 2e-3;
+* out: the combine stage-isolated and the whole layer end to end, 2e-3.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp4_block_scaled_amd import datagen as dg
+from mxfp4_block_scaled_amd import ops
+from tests.helpers import GEMM_TOL, bf16_dev, h_error_bound, host, straddle_check_bound, unpack_codes
+
+pytestmark = pytest.mark.gpu
+
+WORKERS = min(16, len(os.sched_getaffinity(0)))
+
+
+def _unit_rows(offsets, unit, stream_max):
+    """First and last row of every `unit`-row block of every expert; every row of
+    experts with at most `stream_max` rows."""
+    rows = []
+    for e in range(offsets.size - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        if hi - lo <= stream_max:
+            rows.extend(range(lo, hi))
+            continue
+        for u0 in range(lo, hi, unit):
+            rows += [u0, min(u0 + unit, hi) - 1]
+    return sorted(set(rows))
+
+
+def _run_and_check(name, unit, stream_max):
+    d = dg.workload_inputs(name)
+    cfg = d["cfg"]
+    T, k, fmt, E = cfg["T"], cfg["k"], cfg["act_fmt"], cfg["E"]
+    w = (d["w1"], d["s1"], d["w2"], d["s2"])
+    wd = [torch.from_numpy(np.ascontiguousarray(t)).cuda() for t in w]
+    r = ops.moe_layer(bf16_dev(d["x"]), torch.from_numpy(d["logits"]).cuda(), *wd, topk=k, act_fmt=fmt)
+    torch.cuda.synchronize()
+    small = {key: host(r[key]) for key in ("q", "q_scale", "topk_ids", "gates", "expert_offsets", "sorted_pair",
+                                           "pair_row")}
+    offs = small["expert_offsets"]
+    rows0 = _unit_rows(offs, unit, stream_max)
+    touched = np.nonzero(np.diff(offs))[0]
+    e_of = np.searchsorted(offs, rows0, side="right") - 1
+    assert set(np.unique(e_of)) == set(touched), "some touched expert has no sampled row"
+    tokens = sorted({int(small["sorted_pair"][rr]) // k for rr in rows0})
+    rows = np.array([int(small["pair_row"][t * k + j]) for t in tokens for j in range(k)])
+    ridx = torch.from_numpy(rows).cuda()
+    g = dict(small)
+    g["h"] = host(r["h"].index_select(0, ridx))
+    g["h_scale"] = host(r["h_scale"].index_select(0, ridx))
+    g["y"] = host(r["y"].index_select(0, ridx))
+    tok_t = torch.tensor(tokens, dtype=torch.int64, device="cuda")
+    g["out"] = host(r["out"].index_select(0, tok_t))
+    del r, wd
+    torch.cuda.empty_cache()
+
+    ref = oracle.moe_layer(d["x"], d["logits"], *w, k, fmt, rows=rows, workers=WORKERS, abs_terms=True)
+    for key in ("q", "q_scale", "topk_ids", "expert_offsets", "sorted_pair", "pair_row"):
+        assert np.array_equal(g[key], ref[key]), key
+    I = ref["h_pre"].shape[1]
+    dh = h_error_bound(ref["G"][rows], ref["G_abs"][rows], I, fmt)
+    n_code, n_scale = straddle_check_bound(unpack_codes(g["h"], fmt), g["h_scale"], ref["h_pre"][rows], dh, fmt)
+    # y, stage-isolated: the oracle's FC2 on the GPU's own h
+    e_of_row = np.searchsorted(offs, rows, side="right") - 1
+    y_ref = np.zeros_like(g["y"])
+    for e in np.unique(e_of_row):
+        sel = e_of_row == e
+        y_ref[sel] = oracle.fc2_rows(g["h"][sel], g["h_scale"][sel], fmt, w[2][e], w[3][e])
+    err_y = oracle.row_normalised_error(g["y"], y_ref)
+    assert err_y <= GEMM_TOL, f"y error {err_y}"
+    # out: combine on the GPU's y (stage-isolated) and end to end, on the owning tokens
+    tok = np.array(tokens)
+    pos = {int(rr): i for i, rr in enumerate(rows)}
+    y_tok = np.stack([np.stack([g["y"][pos[int(g["pair_row"][t * k + j])]] for j in range(k)]) for t in tok])
+    gates = g["gates"][tok].astype(np.float64)
+    comb = np.einsum("tj,tjn->tn", gates, y_tok)
+    err_c = oracle.row_normalised_error(g["out"], comb)
+    assert err_c <= GEMM_TOL, f"combine error {err_c}"
+    err_e = oracle.row_normalised_error(g["out"], ref["out"][tok])
+    assert err_e <= GEMM_TOL, f"end-to-end error {err_e}"
+    print(f"\n[{name}] {touched.size} experts, {len(rows0)} unit rows, {len(tokens)} tokens ({rows.size} rows): "
+          f"h codes off by rounding {n_code}, scale bytes {n_scale}; y {err_y:.2e}, combine {err_c:.2e}, "
+          f"end to end {err_e:.2e}")
+
+
+def test_fp4_prefill_16384_tokens_every_expert():
+    # E2M1 activations: 256-row units of the wide tiled kernel
+    _run_and_check("moe_prefill_t16384_fp4", unit=256, stream_max=0)
+
+
+def test_zipf_prefill_2048_tokens_every_touched_expert():
+    # E4M3 activations: experts of <= 16 rows streamed, the others in 128-row tiles
+    _run_and_check("moe_prefill_t2048_zipf", unit=128, stream_max=16)

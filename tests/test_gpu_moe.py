@@ -1,7 +1,9 @@
 """GPU parity of the MoE expert path: grouped FC1 (+ fused SwiGLU/requantise),
 FC2, combine, stage by stage and end to end, against the fp64 oracle.
 
-* h (requantised SwiGLU output): straddle rule against the oracle's own chain;
+* h (requantised SwiGLU output): every code must be a correct rounding of a value
+  within the per-element error bound of the oracle's exact h (tests/helpers.py:
+  the bound follows from the measured FC1 accumulation residual);
 * y (FC2): stage-isolated - the oracle's FC2 is fed the GPU's own h;
 * out (combine): stage-isolated on the GPU's y, and end to end against the
   fully independent oracle chain; both within 2e-3 row-normalised.
@@ -14,7 +16,7 @@ import torch
 import oracle
 from mxfp4_block_scaled_amd import datagen as dg
 from mxfp4_block_scaled_amd import ops
-from tests.helpers import GEMM_TOL, bf16_dev, host, straddle_check, unpack_codes
+from tests.helpers import GEMM_TOL, bf16_dev, h_error_bound, host, straddle_check_bound, unpack_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +36,10 @@ def _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt, rows=None, tokens=None):
     for key in ("q", "q_scale", "topk_ids", "expert_offsets", "sorted_pair", "pair_row"):
         assert np.array_equal(g[key], ref[key]), key
     rows = np.arange(T * k) if rows is None else np.asarray(rows)
-    # h: straddle rule against the oracle's fp64 pre-quantisation values
-    straddle_check(unpack_codes(g["h"][rows], fmt), g["h_scale"][rows], ref["h_pre"][rows], fmt)
+    # h: the GPU's codes against the oracle's exact values within the error bound
+    I = ref["h_pre"].shape[1]
+    dh = h_error_bound(ref["G"][rows], ref["G_abs"][rows], I, fmt)
+    straddle_check_bound(unpack_codes(g["h"][rows], fmt), g["h_scale"][rows], ref["h_pre"][rows], dh, fmt)
     # y: stage-isolated (oracle FC2 on the GPU's own h)
     e_of_row = np.searchsorted(ref["expert_offsets"], rows, side="right") - 1
     y_ref = np.zeros((rows.size, g["y"].shape[1]))
@@ -72,7 +76,7 @@ def test_layer_small_shapes_full_oracle(T, H, I, E, k, fmt, seed):
     logits = dg.logits(seed, T, E, "normal")
     w1, s1, w2, s2 = dg.moe_weights(seed, E, H, I, 120, 128)
     g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, fmt)
-    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, fmt)
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, fmt, abs_terms=True)
     _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt)
 
 
@@ -83,7 +87,7 @@ def test_layer_skewed_routing_one_expert_takes_all():
     logits[:, 5] += 50.0  # every token's first choice is expert 5 (two full tiles + a tail)
     w1, s1, w2, s2 = dg.moe_weights(11, E, H, I, 120, 128)
     g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, "e4m3")
-    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e4m3")
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e4m3", abs_terms=True)
     _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e4m3")
 
 
@@ -103,7 +107,7 @@ def test_layer_split_small_experts_stream(fmt, y_dtype):
     w1, s1, w2, s2 = dg.moe_weights(15, E, H, I, 120, 128)
     g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, fmt, y_dtype=y_dtype)
     assert np.array_equal(np.diff(g["expert_offsets"]), counts)
-    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, fmt)
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, fmt, abs_terms=True)
     _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt)
 
 
@@ -117,7 +121,7 @@ def test_layer_split_zipf_routing(fmt):
     g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, fmt)
     c = np.diff(g["expert_offsets"])
     assert (c > 16).any() and ((c > 0) & (c <= 16)).any()
-    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, fmt)
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, fmt, abs_terms=True)
     _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt)
 
 
@@ -128,7 +132,7 @@ def test_layer_fp32_y(T):
     logits = dg.logits(12, T, E, "normal")
     w1, s1, w2, s2 = dg.moe_weights(12, E, H, I, 120, 128)
     g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, "e4m3", y_dtype=torch.float32)
-    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e4m3")
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e4m3", abs_terms=True)
     _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e4m3")
 
 
@@ -139,7 +143,7 @@ def test_layer_fp32_y_fp8_tiles():
     logits = dg.logits(14, T, E, "normal")
     w1, s1, w2, s2 = dg.moe_weights(14, E, H, I, 120, 128)
     g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, "e4m3", y_dtype=torch.float32)
-    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e4m3")
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e4m3", abs_terms=True)
     _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e4m3")
 
 
@@ -150,51 +154,19 @@ def test_layer_fp32_y_fp4_tiles(I):
     logits = dg.logits(13, T, E, "normal")
     w1, s1, w2, s2 = dg.moe_weights(13, E, H, I, 120, 128)
     g = _layer(x, logits, _dev_weights(w1, s1, w2, s2), k, "e2m1", y_dtype=torch.float32)
-    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e2m1")
+    ref = oracle.moe_layer(x, logits, w1, s1, w2, s2, k, "e2m1", abs_terms=True)
     _compare(g, ref, x, logits, w1, s1, w2, s2, k, "e2m1")
 
 
-@pytest.mark.parametrize("name,ntok", [("moe_decode_t8", None), ("moe_prefill_t2048_zipf", 6),
-                                        ("moe_prefill_t16384_fp4", 4)])
-def test_layer_workloads(name, ntok):
-    """Full-size layers; the oracle computes every row (decode) or the rows of a
-    token sample (prefill), including tokens routed to the hottest expert."""
-    d = dg.workload_inputs(name)
+def test_decode_workload_every_row():
+    """The full-size 8-token decode layer; the oracle computes every row."""
+    d = dg.workload_inputs("moe_decode_t8")
     cfg = d["cfg"]
     k, fmt = cfg["k"], cfg["act_fmt"]
     w = (d["w1"], d["s1"], d["w2"], d["s2"])
     g = _layer(d["x"], d["logits"], _dev_weights(*w), k, fmt)
-    if ntok is None:
-        ref = oracle.moe_layer(d["x"], d["logits"], *w, k, fmt)
-        _compare(g, ref, d["x"], d["logits"], *w, k, fmt)
-        return
-    T = cfg["T"]
-    rng = np.random.default_rng(7)
-    tokens = [0, T - 1] + list(rng.choice(np.arange(1, T - 1), ntok - 2, replace=False))
-    rows = [int(g["pair_row"][t * k + j]) for t in tokens for j in range(k)]
-    ref = oracle.moe_layer(d["x"], d["logits"], *w, k, fmt, rows=rows)
-    _compare(g, ref, d["x"], d["logits"], *w, k, fmt, rows=rows, tokens=tokens)
-
-
-def test_skewed_workload_streamed_and_tiled_experts():
-    """The full-size Zipf-routed layer runs its experts of at most 16 rows in the
-    streaming kernels and the others in tiles: sample tokens with pairs in both."""
-    name = "moe_prefill_t2048_zipf"
-    d = dg.workload_inputs(name)
-    cfg = d["cfg"]
-    k, fmt, T = cfg["k"], cfg["act_fmt"], cfg["T"]
-    w = (d["w1"], d["s1"], d["w2"], d["s2"])
-    g = _layer(d["x"], d["logits"], _dev_weights(*w), k, fmt)
-    counts = np.diff(g["expert_offsets"])
-    ids = g["topk_ids"].reshape(T, k)
-    small = (counts > 0) & (counts <= 16)
-    assert small.any() and (counts > 16).any()
-    has_small = np.nonzero(small[ids].any(axis=1))[0]
-    all_large = np.nonzero(~small[ids].any(axis=1))[0]
-    tokens = [int(t) for t in has_small[:4]] + [int(t) for t in all_large[:2]]
-    rows = [int(g["pair_row"][t * k + j]) for t in tokens for j in range(k)]
-    ref = oracle.moe_layer(d["x"], d["logits"], *w, k, fmt, rows=rows)
-    _compare(g, ref, d["x"], d["logits"], *w, k, fmt, rows=rows, tokens=tokens)
+    ref = oracle.moe_layer(d["x"], d["logits"], *w, k, fmt, workers=8, abs_terms=True)
+    _compare(g, ref, d["x"], d["logits"], *w, k, fmt)
 
 
 def test_layer_is_deterministic():

@@ -174,3 +174,31 @@ def test_row_normalised_error():
     got = np.array([[3.0, 4.5], [0.0, 0.1]])
     assert oracle.row_normalised_error(got, ref) == pytest.approx(0.1)
     assert oracle.row_normalised_error(got[:1], ref[:1]) == pytest.approx(0.1)
+
+
+def test_threaded_layer_equals_serial_and_abs_terms_brute_force():
+    """workers > 1 runs the same per-expert arithmetic on threads: bit-identical
+    results. G_abs = sum_k |a_k w_k| against a plain loop over k, and the triangle
+    inequality |G| <= G_abs with equality when every product is non-negative."""
+    T, H, I, E, k = 6, 64, 32, 4, 2
+    x = dg.activations(3, T, H)
+    L = dg.logits(3, T, E, "normal")
+    w1, s1, w2, s2 = dg.moe_weights(3, E, H, I, 124, 130)
+    a = oracle.moe_layer(x, L, w1, s1, w2, s2, k, "e4m3", abs_terms=True)
+    b = oracle.moe_layer(x, L, w1, s1, w2, s2, k, "e4m3", workers=3, abs_terms=True)
+    for key in ("G", "G_abs", "h_pre", "h", "h_scale", "y", "out"):
+        assert np.array_equal(a[key], b[key], equal_nan=True), key
+    q_hat = oracle.moe.decode_act(a["q"], a["q_scale"], "e4m3")
+    for r in range(T * k):
+        t = int(a["sorted_pair"][r]) // k
+        e = int(np.searchsorted(a["expert_offsets"], r, side="right") - 1)
+        W = oracle.dequant_weights(w1[e], s1[e])
+        for n in (0, 5, 2 * I - 1):
+            s = 0.0
+            for kk in range(H):
+                s += abs(q_hat[t, kk] * W[n, kk])
+            assert math.isclose(a["G_abs"][r, n], s, rel_tol=1e-12)
+    assert np.all(np.abs(a["G"]) <= a["G_abs"] * (1 + 1e-12))
+    pos = oracle.fc1_abs_terms(np.abs(q_hat[:2]), np.full((3, H // 2), 0x22, np.uint8),
+                               np.full((3, H // 32), 127, np.uint8))
+    assert np.allclose(pos, np.abs(q_hat[:2]).sum(1)[:, None], rtol=1e-15)
