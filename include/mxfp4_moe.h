@@ -73,6 +73,14 @@ int mxf_abi_version(void);
 
 /*
  * mxfp4_quantize_act - quantise activation rows per 32-element block.
+ * Defined by: the activation side of the FP4 path, page "DGX Spark 原生 FP4 矩阵
+ * 指令" sections 一 (E2M1 elements with one UE8M0 scale per block, fed to the
+ * matrix instruction as they are) and 二 (activations kept in FP4 end to end on the
+ * FP4 path); the FP8 activations of the grouped FP8 x FP4 GEMM, page "【DeepSeek
+ * V4】Triton FP4 优化实战" section 第零步 (the profiled m_grouped_fp8_fp4 call); and
+ * the "FP8 quant" step of page "Domestic GPUs are awesome! ... DeepSeek-V4". The
+ * block rule itself (floor(log2 amax) - emax, round to nearest even) is the OCP MX
+ * one stated at the top of this header.
  *   x        [rows][K] bf16 (x_dtype = MXF_BF16) or fp32 (MXF_F32) values
  *   fmt      MXF_E4M3 -> q [rows][K] ; MXF_E2M1 -> q [rows][K/2] (packed)
  *   q_scale  [rows][K/32] UE8M0 bytes
@@ -84,7 +92,10 @@ int mxfp4_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t K, int 
 
 /*
  * mxfp4_gemm - dense MXFP4 GEMM, C = A_hat * W_hat^T
- * (the dense MXFP4 entry of page "DGX Spark 原生 FP4 矩阵指令" section 二).
+ * Defined by: the dense MXFP4 entry of page "DGX Spark 原生 FP4 矩阵指令" section 二,
+ * the K-shape guard of its section 三 (a K the kernels cannot take is an error, never
+ * a silent other path), and the dense shapes of the accuracy table in page "【DeepSeek
+ * V4】Triton FP4 优化实战" section 第二步 (16 x 32 x 4096 and 64 x 4096 x 7168).
  *   a        [M][K] bf16 activations, quantised inside the call per 32-block to
  *            act_fmt (E4M3 or E2M1) with the rule above; the quantised copy
  *            lives only in `workspace`
@@ -110,6 +121,12 @@ int mxfp4_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K, int act_fmt,
 
 /*
  * moe_route_permute - top-k routing and the expert-grouped permutation.
+ * Defined by: page "【DeepSeek V4】Triton FP4 优化实战" section "FP4 MoE GEMM 是什么？"
+ * (each token picks 6 of 256 experts) and page "Domestic GPUs are awesome! ...
+ * DeepSeek-V4" (MoE routing / Top-k as an operator, and the dispatch that groups a
+ * token's rows by expert before the expert GEMMs); the grouped, row-contiguous
+ * layout is the one of the profiled m_grouped_..._contiguous call in the Triton
+ * page's section 第零步.
  *   logits         [T][E] fp32
  *   topk_ids       [T][topk] i32: per token the topk largest logits, distinct
  *                  experts, ordered by (logit descending, expert index ascending)
@@ -130,6 +147,11 @@ int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t topk,
 
 /*
  * moe_grouped_mxfp4_gemm - both expert FCs for every (token, expert) pair.
+ * Defined by: page "DGX Spark 原生 FP4 矩阵指令" section 二 (the MoE MXFP4 entry;
+ * weights stay FP4 into the matrix instruction), page "【DeepSeek V4】Triton FP4
+ * 优化实战" sections "FP4 MoE GEMM 是什么？" (two FC per expert) and 第二步 (expert
+ * FC1 is 4096 x 7168; even column in the low nibble), and page "Domestic GPUs are
+ * awesome! ... DeepSeek-V4" ("SwiGLU + FP8 quant" fused between the two FCs).
  *   q, q_scale     quantised layer input [T][H] (E4M3) or [T][H/2] (E2M1) + [T][H/32]
  *   act_fmt        element format of q and of h
  *   expert_offsets, sorted_pair  as written by moe_route_permute
@@ -156,6 +178,9 @@ int moe_grouped_mxfp4_gemm(const uint8_t* q, const uint8_t* q_scale, int act_fmt
 
 /*
  * moe_unpermute_combine - out[t] = sum_{j=0..topk-1} gates[t][j] * y[pair_row[t*topk+j]]
+ * Defined by: the combine half of MoE dispatch/combine, page "Domestic GPUs are
+ * awesome! ... DeepSeek-V4"; the gates are the routing weights of page "【DeepSeek
+ * V4】Triton FP4 优化实战" section "FP4 MoE GEMM 是什么？".
  * accumulated in fp32 in slot order j = 0, 1, ..., then stored as out_dtype
  * (bf16: round to nearest even). y [T*topk][H] (y_dtype), out [T][H].
  * Requires H % 8 == 0. Errors: NULL, SHAPE, ALIGN, FORMAT.
