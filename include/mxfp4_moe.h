@@ -120,6 +120,29 @@ int mxfp4_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K, int act_fmt,
                void* workspace, size_t workspace_bytes, mxf_stream stream);
 
 /*
+ * mxfp4_gemm_noalloc - mxfp4_gemm with its workspace inside the library.
+ * For callers that cannot allocate device memory or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation. The
+ * result is that of mxfp4_gemm (the same kernels, bit for bit).
+ *   The workspace is a fixed device array of MXF_NOALLOC_SCRATCH_BYTES (16 MiB) per
+ *   GPU, held from the library's first use on that GPU until the process ends; its
+ *   device address is looked up once per device on the first call made with that
+ *   device current. Nothing is allocated or freed by any call.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time on one
+ *   GPU (different streams, or different host threads) race and give undefined
+ *   results; calls ordered on one stream are safe. Nothing in the array needs to
+ *   start at zero (each call overwrites what it reads).
+ * Arguments as for mxfp4_gemm without the workspace pair. A call whose workspace
+ * (mxfp4_gemm_workspace_bytes) exceeds the array returns MXF_ERR_WORKSPACE before
+ * touching the device (the 64 x 4096 x 7168 GEMM needs 4.5 MiB). Other errors as
+ * for mxfp4_gemm; MXF_ERR_LAUNCH also if the array's address cannot be found.
+ */
+#define MXF_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+size_t mxfp4_noalloc_scratch_bytes(void);
+int mxfp4_gemm_noalloc(const uint16_t* a, int64_t M, int64_t N, int64_t K, int act_fmt,
+                       const uint8_t* w, const uint8_t* w_scale, float* c, mxf_stream stream);
+
+/*
  * moe_route_permute - top-k routing and the expert-grouped permutation.
  * Defined by: page "【DeepSeek V4】Triton FP4 优化实战" section "FP4 MoE GEMM 是什么？"
  * (each token picks 6 of 256 experts) and page "Domestic GPUs are awesome! ...

@@ -27,6 +27,8 @@ SIGNATURES = {
     "mxfp4_quantize_act": (_c_int, [_p, _c_int, _c_i64, _c_i64, _c_int, _p, _p, _p]),
     "mxfp4_gemm_workspace_bytes": (_sz, [_c_i64, _c_i64, _c_i64, _c_int]),
     "mxfp4_gemm": (_c_int, [_p, _c_i64, _c_i64, _c_i64, _c_int, _p, _p, _p, _p, _sz, _p]),
+    "mxfp4_noalloc_scratch_bytes": (_sz, []),
+    "mxfp4_gemm_noalloc": (_c_int, [_p, _c_i64, _c_i64, _c_i64, _c_int, _p, _p, _p, _p]),
     "moe_route_permute": (_c_int, [_p, _c_i64, _c_i32, _c_i32, _p, _p, _p, _p, _p, _p]),
     "moe_grouped_mxfp4_gemm": (_c_int, [_p, _p, _c_int, _c_i64, _c_i32, _c_i64, _c_i64, _c_i32,
                                         _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_int, _p]),
@@ -137,6 +139,24 @@ def mxfp4_gemm(a, w, w_scale, act_fmt="e4m3", out=None, workspace=None):
     _check(lib.mxfp4_gemm(_ptr(a), M, N, K, f, _ptr(w), _ptr(w_scale), _ptr(c), _ptr(workspace),
                           workspace.numel(), _stream(dev)), "mxfp4_gemm")
     return c
+
+
+def mxfp4_gemm_noalloc(a, w, w_scale, out, act_fmt="e4m3"):
+    """mxfp4_gemm with the library's own fixed workspace (no allocation in the call):
+    a [M][K] bf16, w [N][K/2] uint8, w_scale [N][K/32] uint8 -> out [M][N] fp32."""
+    dev = _dev(a)
+    _dev(w), _dev(w_scale), _dev(out)
+    if a.dim() != 2 or w.dim() != 2:
+        raise RuntimeError("a must be [M][K] and w [N][K/2]")
+    M, K = a.shape
+    N = w.shape[0]
+    _need(a, "a", torch.bfloat16, (M, K))
+    _need(w, "w", torch.uint8, (N, K // 2))
+    _need(w_scale, "w_scale", torch.uint8, (N, K // 32))
+    _need(out, "out", torch.float32, (M, N))
+    _check(load().mxfp4_gemm_noalloc(_ptr(a), M, N, K, FMTS[act_fmt], _ptr(w), _ptr(w_scale), _ptr(out),
+                                     _stream(dev)), "mxfp4_gemm_noalloc")
+    return out
 
 
 def moe_route_permute(logits, topk):

@@ -158,3 +158,16 @@ def test_ceiling_probe_errors():
     assert lib.mxf_ceiling_read(None, 64, A, None) == NULL
     assert lib.mxf_ceiling_read(U, 64, A, None) == ALIGN
     assert lib.mxf_ceiling_read(None, 0, None, None) == OK
+
+
+def test_noalloc_gemm_rejects_before_touching_the_device():
+    """Validation and the size limit come before any HIP call."""
+    lib = _lib()
+    cap = lib.mxfp4_noalloc_scratch_bytes()
+    assert cap == 16 << 20
+    assert lib.mxfp4_gemm_noalloc(A, 8192, 256, 4096, 0, A, A, A, None) == WORKSPACE   # 32 MiB of quantised A
+    assert lib.mxfp4_gemm_noalloc(A, 16, 256, 4000, 0, A, A, A, None) == SHAPE         # K % 512
+    assert lib.mxfp4_gemm_noalloc(A, 16, 24, 4096, 0, A, A, A, None) == SHAPE          # N % 16
+    assert lib.mxfp4_gemm_noalloc(A, 16, 256, 4096, 9, A, A, A, None) == FORMAT
+    assert lib.mxfp4_gemm_noalloc(None, 16, 256, 4096, 0, A, A, A, None) == NULL
+    assert lib.mxfp4_gemm_noalloc(A, 0, 256, 4096, 0, A, A, A, None) == OK             # M == 0: no-op
