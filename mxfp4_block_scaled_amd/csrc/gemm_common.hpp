@@ -176,6 +176,15 @@ __device__ __forceinline__ void grouped_work_item(const int32_t* __restrict__ of
   loc_out = (int)(local % ke);
 }
 
+// f(integral_constant<int, i>) for i = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // silu(g) * u with the hardware exponential and reciprocal (about 1 ulp each)
 __device__ __forceinline__ float silu_mul(float g, float u) {
 #if defined(__HIP_DEVICE_COMPILE__)

@@ -173,13 +173,6 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& a, const v16f (&ac
 
 // NST > 0: K / 256 is a compile-time constant and the ring is fully unrolled;
 // NST == 0: any K (multiple of 256) with a runtime loop.
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
 
 // NTG: consecutive n-tiles per workgroup (grouped GEMMs in the expert-major order;
 // 1 for dense), unrolled like the stages
