@@ -143,6 +143,38 @@ int mxfp4_gemm_noalloc(const uint16_t* a, int64_t M, int64_t N, int64_t K, int a
                        const uint8_t* w, const uint8_t* w_scale, float* c, mxf_stream stream);
 
 /*
+ * mxfp4_gemm_w4a16 / nvfp4_gemm_w4a16 - FP4 weights x bf16 activations:
+ *   C[M][N] (fp32) = A . W_hat^T, A [M][K] bf16 used as given (no activation
+ *   quantisation), fp32 accumulation.
+ * Defined by: the fused dequantise + matmul of page "【DeepSeek V4】Triton FP4 优化实战"
+ * section 第二步 (packed FP4 weights, even column in the low nibble, turned into bf16
+ * inside the kernel and multiplied in bf16, no 16-bit weight copy in memory), with its
+ * accuracy table's shapes (1 x 32 x 4096, 1 x 4096 x 7168, 64 x 4096 x 7168); the
+ * NVFP4 block format is the one of the kind::mxf4nvf4 / scale_vec::4X instruction of page
+ * "DGX Spark 原生 FP4 矩阵指令" section 一 (E2M1 codes, a UE4M3 scale per 16 elements).
+ *   w        [N][K/2] E2M1 codes, element 2n in the low nibble of byte n
+ *   w_scale  mxfp4: [N][K/32] UE8M0 bytes, value 2^(byte - 127), bytes 2 .. 252 (every
+ *            decoded weight then lies in bf16's normal range; smaller bytes give weights
+ *            the bf16 instruction may flush, larger ones overflow bf16);
+ *            nvfp4: [N][K/16] UE4M3 bytes (OCP E4M3 with the sign bit clear), value
+ *            2^(e-7) (1 + m/8), or m 2^-9 for e = 0; 0x7F (NaN) is not a valid scale
+ *   c        [M][N] fp32
+ *   workspace, workspace_bytes: device scratch of at least fp4_w4a16_workspace_bytes(M,
+ *            N, K) bytes (0 means none needed; 16-byte aligned): fp32 partial sums of
+ *            the K slices, added in a fixed order (bit-identical results run to run).
+ * Every weight value code x scale is exact in bf16, so the only rounding is the fp32
+ * accumulation. Requires K % 512 == 0, N % 16 == 0, M >= 0 (0 is a no-op), K < 2^27.
+ * Errors: NULL, SHAPE, ALIGN, WORKSPACE, UNSUPPORTED.
+ */
+size_t fp4_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int mxfp4_gemm_w4a16(const uint16_t* a, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+                     const uint8_t* w_scale, float* c, void* workspace, size_t workspace_bytes,
+                     mxf_stream stream);
+int nvfp4_gemm_w4a16(const uint16_t* a, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+                     const uint8_t* w_scale, float* c, void* workspace, size_t workspace_bytes,
+                     mxf_stream stream);
+
+/*
  * moe_route_permute - top-k routing and the expert-grouped permutation.
  * Defined by: page "【DeepSeek V4】Triton FP4 优化实战" section "FP4 MoE GEMM 是什么？"
  * (each token picks 6 of 256 experts) and page "Domestic GPUs are awesome! ...

@@ -82,6 +82,41 @@ int mxfp4_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K, int act_fmt, 
   return MXF_OK;
 }
 
+size_t fp4_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const int S = mxf::w4a16_ksplit(M, N, K);
+  const int64_t mm = M < 64 ? M : 64;
+  return S > 1 ? round_up((size_t)S * (size_t)mm * (size_t)N * sizeof(float), 256) : 0;
+}
+
+namespace {
+int w4a16_call(bool nvfp4, const uint16_t* a, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+               const uint8_t* w_scale, float* c, void* workspace, size_t workspace_bytes, mxf_stream stream) {
+  if (M < 0 || M > kMaxRows || N <= 0 || N % 16 != 0 || K <= 0 || K % 512 != 0) return MXF_ERR_SHAPE;
+  // 64 weight rows of a workgroup are addressed with 32-bit offsets
+  if (64 * (K / 2) >= ((int64_t)1 << 32)) return MXF_ERR_UNSUPPORTED;
+  if (M == 0) return MXF_OK;
+  if (!a || !w || !w_scale || !c) return MXF_ERR_NULL;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(w_scale) || !aligned16(c)) return MXF_ERR_ALIGN;
+  const size_t need = fp4_w4a16_workspace_bytes(M, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MXF_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return MXF_ERR_ALIGN;
+  const int rc = mxf::launch_w4a16_gemm(nvfp4, a, M, N, K, w, w_scale, c, static_cast<float*>(workspace),
+                                        as_stream(stream));
+  return rc ? MXF_ERR_LAUNCH : MXF_OK;
+}
+}  // namespace
+
+int mxfp4_gemm_w4a16(const uint16_t* a, int64_t M, int64_t N, int64_t K, const uint8_t* w, const uint8_t* w_scale,
+                     float* c, void* workspace, size_t workspace_bytes, mxf_stream stream) {
+  return w4a16_call(false, a, M, N, K, w, w_scale, c, workspace, workspace_bytes, stream);
+}
+
+int nvfp4_gemm_w4a16(const uint16_t* a, int64_t M, int64_t N, int64_t K, const uint8_t* w, const uint8_t* w_scale,
+                     float* c, void* workspace, size_t workspace_bytes, mxf_stream stream) {
+  return w4a16_call(true, a, M, N, K, w, w_scale, c, workspace, workspace_bytes, stream);
+}
+
 int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* topk_ids, float* gates,
                       int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_row, mxf_stream stream) {
   if (T < 0 || E < 1 || topk < 1 || topk > 8 || topk > E) return MXF_ERR_SHAPE;

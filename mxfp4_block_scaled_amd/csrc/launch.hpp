@@ -34,6 +34,12 @@ int launch_dense_gemm(const uint8_t* qa, const uint8_t* qa_scale, bool act_fp4, 
                       int64_t K, const uint8_t* w, const uint8_t* w_scale, float* c, float* partials,
                       hipStream_t stream);
 
+// FP4 weights x bf16 activations (gemm_w4a16.hip): K slices of 4 super-steps for narrow N
+// (w4a16_ksplit > 1 needs w4a16_ksplit * min(M, 64) * N fp32 of partial sums)
+int w4a16_ksplit(int64_t M, int64_t N, int64_t K);
+int launch_w4a16_gemm(bool nvfp4, const uint16_t* a, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+                      const uint8_t* ws, float* c, float* partials, hipStream_t stream);
+
 int launch_grouped_gemm(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, int64_t T, int topk,
                         int64_t H, int64_t I, int E, const int32_t* expert_offsets,
                         const int32_t* sorted_pair, const uint8_t* w1, const uint8_t* w1_scale,

@@ -12,7 +12,7 @@ touched.
 Tags: 1 activations (standard normal fp32), 2 outlier mask (p = 0.01),
 3 routing logits (standard normal fp32), 4 / 5 dense weight codes / scale
 exponents, 6 / 7 FC1 codes / scale exponents per expert, 8 / 9 FC2 codes /
-scale exponents per expert.
+scale exponents per expert, 10 / 11 NVFP4 weight codes / UE4M3 scale fields.
 
 Workloads (shapes of the pages' DeepSeek-V4-Flash expert layer: 256 experts,
 top-6, expert FC1 4096 x 7168 (gate||up) and FC2 7168 x 2048; and the dense
@@ -24,6 +24,7 @@ import numpy as np
 TAG_ACT, TAG_OUTLIER, TAG_LOGITS = 1, 2, 3
 TAG_DENSE_W, TAG_DENSE_S = 4, 5
 TAG_W1, TAG_S1, TAG_W2, TAG_S2 = 6, 7, 8, 9
+TAG_NV_W, TAG_NV_S = 10, 11
 
 WORKLOADS = {
     # dense MXFP4 GEMM, bf16 activations quantised inside the call to E4M3
@@ -88,6 +89,17 @@ def dense_weights(seed, N, K, exp_lo, exp_hi):
     w = _random_bytes(rng(seed, TAG_DENSE_W), (N, K // 2))
     s = _scale_bytes(rng(seed, TAG_DENSE_S), (N, K // 32), exp_lo, exp_hi)
     return w, s
+
+
+def nvfp4_weights(seed, N, K, e_lo=4, e_hi=10):
+    """NVFP4 weights: packed E2M1 codes [N][K/2] (uniform over all 16 codes per nibble)
+    and one UE4M3 scale byte per 16 elements [N][K/16]: exponent field uniform in
+    [e_lo, e_hi], mantissa field uniform in 0..7, sign bit clear."""
+    w = _random_bytes(rng(seed, TAG_NV_W), (N, K // 2))
+    g = rng(seed, TAG_NV_S)
+    e = g.integers(e_lo, e_hi + 1, size=(N, K // 16), dtype=np.uint8)
+    m = g.integers(0, 8, size=(N, K // 16), dtype=np.uint8)
+    return w, ((e << 3) | m).astype(np.uint8)
 
 
 def expert_weights(seed, e, H, I, exp_lo, exp_hi, out=None):

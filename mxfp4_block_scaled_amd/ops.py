@@ -29,6 +29,9 @@ SIGNATURES = {
     "mxfp4_gemm": (_c_int, [_p, _c_i64, _c_i64, _c_i64, _c_int, _p, _p, _p, _p, _sz, _p]),
     "mxfp4_noalloc_scratch_bytes": (_sz, []),
     "mxfp4_gemm_noalloc": (_c_int, [_p, _c_i64, _c_i64, _c_i64, _c_int, _p, _p, _p, _p]),
+    "fp4_w4a16_workspace_bytes": (_sz, [_c_i64, _c_i64, _c_i64]),
+    "mxfp4_gemm_w4a16": (_c_int, [_p, _c_i64, _c_i64, _c_i64, _p, _p, _p, _p, _sz, _p]),
+    "nvfp4_gemm_w4a16": (_c_int, [_p, _c_i64, _c_i64, _c_i64, _p, _p, _p, _p, _sz, _p]),
     "moe_route_permute": (_c_int, [_p, _c_i64, _c_i32, _c_i32, _p, _p, _p, _p, _p, _p]),
     "moe_grouped_mxfp4_gemm": (_c_int, [_p, _p, _c_int, _c_i64, _c_i32, _c_i64, _c_i64, _c_i32,
                                         _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_int, _p]),
@@ -157,6 +160,35 @@ def mxfp4_gemm_noalloc(a, w, w_scale, out, act_fmt="e4m3"):
     _check(load().mxfp4_gemm_noalloc(_ptr(a), M, N, K, FMTS[act_fmt], _ptr(w), _ptr(w_scale), _ptr(out),
                                      _stream(dev)), "mxfp4_gemm_noalloc")
     return out
+
+
+def fp4_gemm_w4a16(a, w, w_scale, fmt="mxfp4", out=None, workspace=None):
+    """FP4 weights x bf16 activations: a [M][K] bf16, w [N][K/2] uint8, w_scale [N][K/32]
+    (fmt "mxfp4", UE8M0) or [N][K/16] (fmt "nvfp4", UE4M3) uint8 -> c [M][N] fp32."""
+    dev = _dev(a)
+    _dev(w), _dev(w_scale)
+    if a.dim() != 2 or w.dim() != 2:
+        raise RuntimeError("a must be [M][K] and w [N][K/2]")
+    M, K = a.shape
+    N = w.shape[0]
+    if fmt not in ("mxfp4", "nvfp4"):
+        raise RuntimeError(f"unknown weight format {fmt!r}")
+    _need(a, "a", torch.bfloat16, (M, K))
+    _need(w, "w", torch.uint8, (N, K // 2))
+    _need(w_scale, "w_scale", torch.uint8, (N, K // (16 if fmt == "nvfp4" else 32)))
+    lib = load()
+    need = lib.fp4_w4a16_workspace_bytes(M, N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace)
+    _need(workspace, "workspace", torch.uint8, ((">=", need),))
+    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    _dev(c)
+    _need(c, "out", torch.float32, (M, N))
+    fn = lib.nvfp4_gemm_w4a16 if fmt == "nvfp4" else lib.mxfp4_gemm_w4a16
+    _check(fn(_ptr(a), M, N, K, _ptr(w), _ptr(w_scale), _ptr(c), _ptr(workspace), workspace.numel(), _stream(dev)),
+           f"{fmt}_gemm_w4a16")
+    return c
 
 
 def moe_route_permute(logits, topk):

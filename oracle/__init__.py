@@ -45,9 +45,12 @@ from .mx import (  # noqa: F401
     mx_quantize,
     mx_dequantize,
     dequant_weights,
+    ue4m3_decode,
+    dequant_nvfp4_weights,
 )
 from .moe import (  # noqa: F401
     dense_gemm,
+    w4a16_gemm,
     route_topk,
     permute,
     swiglu,

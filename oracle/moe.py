@@ -24,6 +24,7 @@ import numpy as np
 
 from .mx import (
     FMT_E2M1,
+    dequant_nvfp4_weights,
     FMT_E4M3,
     bf16_bits_to_f64,
     dequant_weights,
@@ -58,6 +59,16 @@ def dense_gemm(a_bf16, w, w_scale, act_fmt=FMT_E4M3):
     a_hat = decode_act(q, qs, act_fmt)
     w_hat = dequant_weights(w, w_scale)
     return a_hat @ w_hat.T, q, qs
+
+
+def w4a16_gemm(a_bf16, w, w_scale, fmt="mxfp4"):
+    """C = A @ W_hat^T in fp64 with the activations as given (bf16, not quantised) and
+    FP4 weights dequantised exactly [TRITON-FP4, "第二步": the fused dequantise + matmul;
+    DS4-FP4 section 一 for the NVFP4 block format]. fmt "mxfp4": w_scale [N][K/32]
+    UE8M0; "nvfp4": w_scale [N][K/16] UE4M3."""
+    a = bf16_bits_to_f64(a_bf16)
+    w_hat = dequant_nvfp4_weights(w, w_scale) if fmt == "nvfp4" else dequant_weights(w, w_scale)
+    return a @ w_hat.T
 
 
 def route_topk(logits, k):

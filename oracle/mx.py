@@ -163,3 +163,22 @@ def mx_dequantize(codes, scales, fmt):
 def dequant_weights(packed, scales):
     """MXFP4 weights [N][K/2] packed + [N][K/32] scales -> fp64 [N][K]."""
     return mx_dequantize(unpack_e2m1(packed), scales, FMT_E2M1)
+
+
+def ue4m3_decode(b):
+    """UE4M3 block-scale bytes -> fp64 [DS4-FP4 section 一: the NVFP4 (kind::mxf4nvf4)
+    scale]. Reading (the page names the type only): an OCP E4M3FN byte with the sign
+    bit clear - exponent 0 subnormal (m * 2^-9), otherwise 2^(e-7) (1 + m/8); 0x7F is
+    NaN; bytes with the sign bit set are not UE4M3 and decode to NaN here."""
+    b = np.asarray(b, dtype=np.uint8)
+    v = _E4M3_TABLE[b & 0x7F]
+    return np.where(b & 0x80, np.nan, v)
+
+
+def dequant_nvfp4_weights(packed, scales16):
+    """NVFP4 weights [N][K/2] packed E2M1 + [N][K/16] UE4M3 scales -> fp64 [N][K]:
+    value = e2m1(code) * ue4m3(scale of its 16-element block)."""
+    codes = unpack_e2m1(packed)
+    K = codes.shape[-1]
+    vals = e2m1_decode(codes).reshape(codes.shape[:-1] + (K // 16, 16))
+    return (vals * ue4m3_decode(scales16)[..., None]).reshape(codes.shape)

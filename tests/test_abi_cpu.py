@@ -171,3 +171,19 @@ def test_noalloc_gemm_rejects_before_touching_the_device():
     assert lib.mxfp4_gemm_noalloc(A, 16, 256, 4096, 9, A, A, A, None) == FORMAT
     assert lib.mxfp4_gemm_noalloc(None, 16, 256, 4096, 0, A, A, A, None) == NULL
     assert lib.mxfp4_gemm_noalloc(A, 0, 256, 4096, 0, A, A, A, None) == OK             # M == 0: no-op
+
+
+def test_w4a16_errors_before_any_device_call():
+    lib = _lib()
+    for fn in (lib.mxfp4_gemm_w4a16, lib.nvfp4_gemm_w4a16):
+        assert fn(A, 4, 64, 1000, A, A, A, A, 1 << 20, None) == SHAPE      # K % 512
+        assert fn(A, 4, 40, 1024, A, A, A, A, 1 << 20, None) == SHAPE      # N % 16
+        assert fn(A, -1, 64, 1024, A, A, A, A, 1 << 20, None) == SHAPE
+        assert fn(A, 0, 64, 1024, A, A, A, A, 0, None) == OK               # M == 0: no-op
+        assert fn(None, 4, 64, 1024, A, A, A, A, 1 << 20, None) == NULL
+        assert fn(U, 4, 64, 1024, A, A, A, A, 1 << 20, None) == ALIGN
+        need = lib.fp4_w4a16_workspace_bytes(4, 64, 4096)                   # narrow N: K slices
+        assert need > 0
+        assert fn(A, 4, 64, 4096, A, A, A, A, need - 1, None) == WORKSPACE
+        assert fn(A, 4, 64, 4096, A, A, A, None, need, None) == WORKSPACE
+    assert lib.fp4_w4a16_workspace_bytes(4, 16384, 4096) == 0            # wide N: no K split
