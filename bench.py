@@ -11,7 +11,8 @@ Also reported on the same line: the 8-token decode layer (weight GB/s over the
 touched experts) and the dense 64 x 4096 x 7168 GEMM, each against its roofline.
 The fp64 CPU oracle is timed on a bounded sample of the headline workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|decode|dense|copy]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                       [--only prefill|decode|dense|skewed|variants|copy]
 
 --only copy runs a plain device-to-device copy of 1 GiB per step (no JSON line):
 the reference kernel of known byte count that scales the FETCH_SIZE / WRITE_SIZE
@@ -257,6 +258,61 @@ def bench_dense(steps, warmup, rotate=48):
     return dict(ms=ms, graph_ms=graph_ms, wbytes=wbytes, gbs=wbytes / (ms * 1e-3) / 1e9, flops=2 * M * N * K)
 
 
+def bench_fp4_variants(steps, warmup, rotate=48):
+    """The FP4-weight GEMMs beside the MX path at the pages' accuracy-table shapes:
+    bf16 activations with MXFP4 or NVFP4 weights, and the lookup-table route (Q8
+    activations, int8-expanded MXFP4 weights; its activation quantisation timed on its
+    own). Weight sets rotate (48 x ~15 MB, beyond the 256 MB cache) so the weights come
+    from HBM; value = weight (+ scale) bytes / call time."""
+    lib = ops.load()
+    out = {}
+    for (M, N, K) in ((1, 4096, 7168), (64, 4096, 7168)):
+        x = bf16_dev(dg.activations(7, M, K, outliers=True))
+        mw, ms = dg.dense_weights(7, N, K, 120, 128)
+        nw, ns = dg.nvfp4_weights(7, N, K)
+        mx = [(to_dev(mw), to_dev(ms))] * 1
+        mx += [(mx[0][0].clone(), mx[0][1].clone()) for _ in range(rotate - 1)]
+        nv = [(to_dev(nw), to_dev(ns))]
+        nv += [(nv[0][0].clone(), nv[0][1].clone()) for _ in range(rotate - 1)]
+        c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(lib.fp4_w4a16_workspace_bytes(M, N, K), 1), dtype=torch.uint8, device="cuda")
+        q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        dq = torch.empty((M, K // 32), dtype=torch.float16, device="cuda")
+        P = ops._ptr
+        it = [0]
+
+        def run(fn, sets):
+            def step(ev):
+                w, s_ = sets[it[0] % len(sets)]
+                it[0] += 1
+                if ev: ev[0].record()
+                ops._check(fn(w, s_), "fp4 variant")
+                if ev: ev[1].record()
+            _, st = time_steps(step, steps * 10, warmup, nev=2)
+            return float(np.mean(st[:, 0]))
+
+        st = ctypes_stream()
+        ms_w16 = run(lambda w, s_: lib.mxfp4_gemm_w4a16(P(x), M, N, K, P(w), P(s_), P(c), P(ws), ws.numel(), st), mx)
+        ms_nv = run(lambda w, s_: lib.nvfp4_gemm_w4a16(P(x), M, N, K, P(w), P(s_), P(c), P(ws), ws.numel(), st), nv)
+        ms_qa = run(lambda w, s_: lib.q8_quantize_act(P(x), M, K, P(q), P(dq), st), mx)
+        ms_q8 = run(lambda w, s_: lib.mxfp4_gemm_q8(P(q), P(dq), M, N, K, P(w), P(s_), P(c), P(ws), ws.numel(), st),
+                    mx)
+        mxb, nvb = N * K // 2 + N * K // 32, N * K // 2 + N * K // 16
+        key = f"m{M}_n{N}_k{K}"
+        out[key] = {
+            "w4a16_mxfp4": {"us": round(ms_w16 * 1e3, 2), "weight_GBps": round(mxb / (ms_w16 * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(mxb / (ms_w16 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "w4a16_nvfp4": {"us": round(ms_nv * 1e3, 2), "weight_GBps": round(nvb / (ms_nv * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(nvb / (ms_nv * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "q8_lut": {"us": round(ms_q8 * 1e3, 2), "quantize_us": round(ms_qa * 1e3, 2),
+                       "weight_GBps": round(mxb / (ms_q8 * 1e-3) / 1e9, 1),
+                       "frac_hbm": round(mxb / (ms_q8 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        }
+        del mx, nv
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_ceilings(reps=3):
     """What this GPU sustains for the two bounds (include/mxf_ceilings.h), best of
     `reps`: a non-temporal streaming read of 2 GiB, and register-only loops of
@@ -340,7 +396,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     # "skewed": the 2048-token Zipf-routed FP8 layer, only when asked for (not in the default line)
-    ap.add_argument("--only", choices=["prefill", "decode", "dense", "skewed", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "dense", "skewed", "variants", "copy"], default=None)
     # the achievable-rate probes run with the default line; with --only, on request
     ap.add_argument("--ceilings", action="store_true")
     args = ap.parse_args()
@@ -439,6 +495,8 @@ def main():
                            "TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
                            "graph": {"ms": round(r["graph_ms"], 5),
                                      "weight_GBps": round(r["wbytes"] / (r["graph_ms"] * 1e-3) / 1e9, 1)}}
+    if args.only in (None, "variants"):
+        result["fp4_variants"] = bench_fp4_variants(args.steps, args.warmup)
     if not args.no_cpu and args.only in (None, "prefill"):
         log("[bench] timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline("moe_prefill_t16384_fp4")

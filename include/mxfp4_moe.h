@@ -175,6 +175,36 @@ int nvfp4_gemm_w4a16(const uint16_t* a, int64_t M, int64_t N, int64_t K, const u
                      mxf_stream stream);
 
 /*
+ * q8_quantize_act / mxfp4_gemm_q8 - the lookup-table route: Q8 activations x MXFP4
+ * weights through int8 products.
+ * Defined by: the generic FP4 path of hardware without FP4 matrix instructions, page
+ * "DGX Spark 原生 FP4 矩阵指令" sections 二 and 三 (FP4 weights expanded to Q8-style
+ * integers, Q8_1-style activations, lossless and with no FP4 speed bonus); the Q8_0
+ * block (32 int8 + an fp16 scale) and the exact FP4 <-> 4-bit lookup-table equivalence,
+ * page "企业官网建设流程全解析" sections 四 and 五.
+ * q8_quantize_act:
+ *   x  [rows][K] bf16; q [rows][K] int8; d [rows][K/32] fp16 (2-byte aligned)
+ *   per 32-block: d = fp16(amax / 127) (fp32 quotient, round to nearest even),
+ *   q = clamp(round_to_nearest_even(x / d), -127, 127) with the quotient in fp32, and
+ *   q = 0 where d = 0. Bit-exact. Requires K % 32 == 0. Errors: NULL, SHAPE, ALIGN.
+ *   (Q8_1's second per-block number, d times the sum of q, serves asymmetric weight
+ *   formats; E2M1 is symmetric, so it is not formed.)
+ * mxfp4_gemm_q8:
+ *   C[M][N] (fp32) = sum over 32-blocks b of (sum_k q[m][k] w8[n][k]) d[m][b] 2^(e - 128)
+ *   where w8 = 2 x e2m1(code) in {0, +-1, +-2, +-3, +-4, +-6, +-8, +-12} (a 16-entry table)
+ *   and e the weight's UE8M0 byte (bytes 2 .. 252): w8 2^(e - 128) is the MXFP4 weight
+ *   exactly. Each block's integer sum is exact; the scaling and the sum over blocks
+ *   round in fp32. q, d as written by q8_quantize_act (d 16-byte aligned here); w, w_scale
+ *   as for mxfp4_gemm; workspace >= mxfp4_gemm_q8_workspace_bytes(M, N, K) (K-slice
+ *   partial sums, added in a fixed order). Requires K % 512 == 0, N % 16 == 0,
+ *   K < 2^27. Errors: NULL, SHAPE, ALIGN, WORKSPACE, UNSUPPORTED.
+ */
+int q8_quantize_act(const uint16_t* x, int64_t rows, int64_t K, int8_t* q, uint16_t* d, mxf_stream stream);
+size_t mxfp4_gemm_q8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int mxfp4_gemm_q8(const int8_t* q, const uint16_t* d, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+                  const uint8_t* w_scale, float* c, void* workspace, size_t workspace_bytes, mxf_stream stream);
+
+/*
  * moe_route_permute - top-k routing and the expert-grouped permutation.
  * Defined by: page "【DeepSeek V4】Triton FP4 优化实战" section "FP4 MoE GEMM 是什么？"
  * (each token picks 6 of 256 experts) and page "Domestic GPUs are awesome! ...

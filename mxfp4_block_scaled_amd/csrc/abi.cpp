@@ -117,6 +117,30 @@ int nvfp4_gemm_w4a16(const uint16_t* a, int64_t M, int64_t N, int64_t K, const u
   return w4a16_call(true, a, M, N, K, w, w_scale, c, workspace, workspace_bytes, stream);
 }
 
+int q8_quantize_act(const uint16_t* x, int64_t rows, int64_t K, int8_t* q, uint16_t* d, mxf_stream stream) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return MXF_ERR_SHAPE;
+  if (rows == 0) return MXF_OK;
+  if (!x || !q || !d) return MXF_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || (reinterpret_cast<uintptr_t>(d) & 1u)) return MXF_ERR_ALIGN;
+  return mxf::launch_q8_quantize(x, rows, K, q, d, as_stream(stream)) ? MXF_ERR_LAUNCH : MXF_OK;
+}
+
+size_t mxfp4_gemm_q8_workspace_bytes(int64_t M, int64_t N, int64_t K) { return fp4_w4a16_workspace_bytes(M, N, K); }
+
+int mxfp4_gemm_q8(const int8_t* q, const uint16_t* d, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+                  const uint8_t* w_scale, float* c, void* workspace, size_t workspace_bytes, mxf_stream stream) {
+  if (M < 0 || M > kMaxRows || N <= 0 || N % 16 != 0 || K <= 0 || K % 512 != 0) return MXF_ERR_SHAPE;
+  if (64 * (K / 2) >= ((int64_t)1 << 32)) return MXF_ERR_UNSUPPORTED;
+  if (M == 0) return MXF_OK;
+  if (!q || !d || !w || !w_scale || !c) return MXF_ERR_NULL;
+  if (!aligned16(q) || !aligned16(d) || !aligned16(w) || !aligned16(w_scale) || !aligned16(c)) return MXF_ERR_ALIGN;
+  const size_t need = mxfp4_gemm_q8_workspace_bytes(M, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MXF_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return MXF_ERR_ALIGN;
+  const int rc = mxf::launch_q8_gemm(q, d, M, N, K, w, w_scale, c, static_cast<float*>(workspace), as_stream(stream));
+  return rc ? MXF_ERR_LAUNCH : MXF_OK;
+}
+
 int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* topk_ids, float* gates,
                       int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_row, mxf_stream stream) {
   if (T < 0 || E < 1 || topk < 1 || topk > 8 || topk > E) return MXF_ERR_SHAPE;

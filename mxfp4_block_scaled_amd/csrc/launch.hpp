@@ -40,6 +40,11 @@ int w4a16_ksplit(int64_t M, int64_t N, int64_t K);
 int launch_w4a16_gemm(bool nvfp4, const uint16_t* a, int64_t M, int64_t N, int64_t K, const uint8_t* w,
                       const uint8_t* ws, float* c, float* partials, hipStream_t stream);
 
+// the lookup-table route (gemm_q8.hip): Q8 activations and int8-expanded MXFP4 weights
+int launch_q8_quantize(const uint16_t* x, int64_t rows, int64_t K, int8_t* q, uint16_t* d, hipStream_t stream);
+int launch_q8_gemm(const int8_t* q, const uint16_t* d, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+                   const uint8_t* ws, float* c, float* partials, hipStream_t stream);
+
 int launch_grouped_gemm(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, int64_t T, int topk,
                         int64_t H, int64_t I, int E, const int32_t* expert_offsets,
                         const int32_t* sorted_pair, const uint8_t* w1, const uint8_t* w1_scale,

@@ -32,6 +32,9 @@ SIGNATURES = {
     "fp4_w4a16_workspace_bytes": (_sz, [_c_i64, _c_i64, _c_i64]),
     "mxfp4_gemm_w4a16": (_c_int, [_p, _c_i64, _c_i64, _c_i64, _p, _p, _p, _p, _sz, _p]),
     "nvfp4_gemm_w4a16": (_c_int, [_p, _c_i64, _c_i64, _c_i64, _p, _p, _p, _p, _sz, _p]),
+    "q8_quantize_act": (_c_int, [_p, _c_i64, _c_i64, _p, _p, _p]),
+    "mxfp4_gemm_q8_workspace_bytes": (_sz, [_c_i64, _c_i64, _c_i64]),
+    "mxfp4_gemm_q8": (_c_int, [_p, _p, _c_i64, _c_i64, _c_i64, _p, _p, _p, _p, _sz, _p]),
     "moe_route_permute": (_c_int, [_p, _c_i64, _c_i32, _c_i32, _p, _p, _p, _p, _p, _p]),
     "moe_grouped_mxfp4_gemm": (_c_int, [_p, _p, _c_int, _c_i64, _c_i32, _c_i64, _c_i64, _c_i32,
                                         _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_int, _p]),
@@ -188,6 +191,47 @@ def fp4_gemm_w4a16(a, w, w_scale, fmt="mxfp4", out=None, workspace=None):
     fn = lib.nvfp4_gemm_w4a16 if fmt == "nvfp4" else lib.mxfp4_gemm_w4a16
     _check(fn(_ptr(a), M, N, K, _ptr(w), _ptr(w_scale), _ptr(c), _ptr(workspace), workspace.numel(), _stream(dev)),
            f"{fmt}_gemm_w4a16")
+    return c
+
+
+def q8_quantize_act(x):
+    """x [rows][K] bf16 -> (q [rows][K] int8, d [rows][K/32] fp16): Q8 blocks of 32."""
+    dev = _dev(x)
+    if x.dim() != 2:
+        raise RuntimeError("x must be [rows][K]")
+    rows, K = x.shape
+    _need(x, "x", torch.bfloat16, (rows, K))
+    q = torch.empty((rows, K), dtype=torch.int8, device=dev)
+    d = torch.empty((rows, K // 32), dtype=torch.float16, device=dev)
+    _check(load().q8_quantize_act(_ptr(x), rows, K, _ptr(q), _ptr(d), _stream(dev)), "q8_quantize_act")
+    return q, d
+
+
+def mxfp4_gemm_q8(q, d, w, w_scale, out=None, workspace=None):
+    """The lookup-table route: q [M][K] int8, d [M][K/32] fp16 (from q8_quantize_act),
+    w [N][K/2] uint8, w_scale [N][K/32] uint8 -> c [M][N] fp32."""
+    dev = _dev(q)
+    for t in (d, w, w_scale):
+        _dev(t)
+    if q.dim() != 2 or w.dim() != 2:
+        raise RuntimeError("q must be [M][K] and w [N][K/2]")
+    M, K = q.shape
+    N = w.shape[0]
+    _need(q, "q", torch.int8, (M, K))
+    _need(d, "d", torch.float16, (M, K // 32))
+    _need(w, "w", torch.uint8, (N, K // 2))
+    _need(w_scale, "w_scale", torch.uint8, (N, K // 32))
+    lib = load()
+    need = lib.mxfp4_gemm_q8_workspace_bytes(M, N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace)
+    _need(workspace, "workspace", torch.uint8, ((">=", need),))
+    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    _dev(c)
+    _need(c, "out", torch.float32, (M, N))
+    _check(lib.mxfp4_gemm_q8(_ptr(q), _ptr(d), M, N, K, _ptr(w), _ptr(w_scale), _ptr(c), _ptr(workspace),
+                             workspace.numel(), _stream(dev)), "mxfp4_gemm_q8")
     return c
 
 

@@ -51,6 +51,9 @@ from .mx import (  # noqa: F401
 from .moe import (  # noqa: F401
     dense_gemm,
     w4a16_gemm,
+    q8_quantize,
+    lut_int8_weights,
+    q8_gemm,
     route_topk,
     permute,
     swiglu,

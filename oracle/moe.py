@@ -25,6 +25,7 @@ import numpy as np
 from .mx import (
     FMT_E2M1,
     dequant_nvfp4_weights,
+    e2m1_decode,
     FMT_E4M3,
     bf16_bits_to_f64,
     dequant_weights,
@@ -69,6 +70,50 @@ def w4a16_gemm(a_bf16, w, w_scale, fmt="mxfp4"):
     a = bf16_bits_to_f64(a_bf16)
     w_hat = dequant_nvfp4_weights(w, w_scale) if fmt == "nvfp4" else dequant_weights(w, w_scale)
     return a @ w_hat.T
+
+
+def q8_quantize(x_bf16):
+    """Q8 activation blocks [DS4-FP4 sections 二/三: Q8_1-style activations on the
+    generic path; FP8-GGUF section 四: a Q8_0 block is 32 int8 plus an fp16 scale].
+    Readings (the pages give the block layout only): per 32-block d = fp16(amax / 127)
+    with the quotient in fp32 and rounded to nearest even, q = x / d in fp32 rounded to
+    nearest even and clamped to [-127, 127], q = 0 where d = 0. The integers are
+    decided in fp32, as the kernel decides them. Returns (q int8 [rows][K],
+    d float16 [rows][K/32])."""
+    x = bf16_bits_to_f64(x_bf16).astype(np.float32)  # exact
+    rows, K = x.shape
+    blk = x.reshape(rows, K // 32, 32)
+    amax = np.abs(blk).max(axis=-1)
+    with np.errstate(over="ignore"):  # amax / 127 beyond fp16's range gives d = inf (then q = 0)
+        d = (amax / np.float32(127.0)).astype(np.float16)
+    d32 = d.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(d32 > 0, np.rint(blk / np.where(d32 > 0, d32, np.float32(1))), np.float32(0))
+    q = np.clip(t, -127, 127).astype(np.int8)
+    return q.reshape(rows, K), d
+
+
+def lut_int8_weights(w):
+    """The 16-entry table [DS4-FP4 section 二; FP8-GGUF section 五: FP4 codes map onto a
+    4-bit lookup-table type]: code -> 2 * e2m1(code), an int8 in {0, +-1, .., +-12};
+    returns int8 [N][K]."""
+    return (2.0 * e2m1_decode(unpack_e2m1(w))).astype(np.int8)
+
+
+def q8_gemm(q, d, w, w_scale):
+    """The lookup-table route in fp64: C[m][n] = sum over blocks b of
+    (sum_k q[m][k] w8[n][k]) * d[m][b] * 2^(e[n][b] - 128), w8 = lut_int8_weights(w)."""
+    q = np.asarray(q, dtype=np.int64)
+    M, K = q.shape
+    w8 = lut_int8_weights(w).astype(np.int64)
+    N = w8.shape[0]
+    da = np.asarray(d, dtype=np.float16).astype(np.float64)
+    dw = np.ldexp(1.0, np.asarray(w_scale, dtype=np.int64) - 128)
+    out = np.zeros((M, N))
+    for b in range(K // 32):
+        ib = q[:, 32 * b:32 * b + 32] @ w8[:, 32 * b:32 * b + 32].T  # exact integers
+        out += ib * da[:, b:b + 1] * dw[None, :, b]
+    return out
 
 
 def route_topk(logits, k):

@@ -187,3 +187,16 @@ def test_w4a16_errors_before_any_device_call():
         assert fn(A, 4, 64, 4096, A, A, A, A, need - 1, None) == WORKSPACE
         assert fn(A, 4, 64, 4096, A, A, A, None, need, None) == WORKSPACE
     assert lib.fp4_w4a16_workspace_bytes(4, 16384, 4096) == 0            # wide N: no K split
+
+
+def test_q8_errors_before_any_device_call():
+    lib = _lib()
+    assert lib.q8_quantize_act(A, 4, 48, A, A, None) == SHAPE          # K % 32
+    assert lib.q8_quantize_act(A, 0, 64, A, A, None) == OK             # rows == 0
+    assert lib.q8_quantize_act(None, 4, 64, A, A, None) == NULL
+    assert lib.q8_quantize_act(A, 4, 64, A, P(4096 + 1), None) == ALIGN  # fp16 scales: 2-byte aligned
+    assert lib.mxfp4_gemm_q8(A, A, 4, 64, 1000, A, A, A, A, 1 << 20, None) == SHAPE
+    assert lib.mxfp4_gemm_q8(A, A, 0, 64, 1024, A, A, A, None, 0, None) == OK
+    assert lib.mxfp4_gemm_q8(A, None, 4, 64, 1024, A, A, A, A, 1 << 20, None) == NULL
+    need = lib.mxfp4_gemm_q8_workspace_bytes(4, 64, 4096)
+    assert need > 0 and lib.mxfp4_gemm_q8(A, A, 4, 64, 4096, A, A, A, A, need - 1, None) == WORKSPACE
