@@ -8,7 +8,10 @@ Headline workload: the 16384-token prefill layer with FP4 x FP4 products
 (hidden 7168, intermediate 2048, 256 experts, top-6, MXFP4 activations),
 value = algorithmic TFLOP/s of the layer (pairs x 88,080,384 flop / step time).
 Also reported on the same line: the 8-token decode layer (weight GB/s over the
-touched experts) and the dense 64 x 4096 x 7168 GEMM, each against its roofline.
+touched experts), the 2048-token Zipf-routed FP8 layer (TFLOP/s and touched-weight
+GB/s), the dense 64 x 4096 x 7168 and 16 x 32 x 4096 GEMMs, and the FP4-weight GEMM
+variants (bf16 activations with MXFP4 / NVFP4 weights, Q8 lookup-table route), each
+against its roofline.
 The fp64 CPU oracle is timed on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
@@ -212,9 +215,9 @@ def bench_moe(name, steps, warmup, rotate):
                 wbytes=wbytes, max_rows=int(counts.max()), layer=layer)
 
 
-def bench_dense(steps, warmup, rotate=48):
-    cfg = dg.WORKLOADS["dense_m64_n4096_k7168"]
-    d = dg.workload_inputs("dense_m64_n4096_k7168")
+def bench_dense(steps, warmup, rotate=48, name="dense_m64_n4096_k7168"):
+    cfg = dg.WORKLOADS[name]
+    d = dg.workload_inputs(name)
     a = bf16_dev(d["a"])
     w0, s0 = to_dev(d["w"]), to_dev(d["w_scale"])
     sets = [(w0, s0)] + [(w0.clone(), s0.clone()) for _ in range(rotate - 1)]
@@ -395,7 +398,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
-    # "skewed": the 2048-token Zipf-routed FP8 layer, only when asked for (not in the default line)
+    # one workload (or the copy reference kernel) instead of the default line
     ap.add_argument("--only", choices=["prefill", "decode", "dense", "skewed", "variants", "copy"], default=None)
     # the achievable-rate probes run with the default line; with --only, on request
     ap.add_argument("--ceilings", action="store_true")
@@ -470,7 +473,7 @@ def main():
         result["decode"] = dec
         del r["layer"]
         torch.cuda.empty_cache()
-    if args.only == "skewed":
+    if args.only in (None, "skewed"):
         name = "moe_prefill_t2048_zipf"
         r = bench_moe(name, args.steps, args.warmup, rotate=1)
         g_ms = r["stage_ms"]["grouped_gemm"]
@@ -489,6 +492,10 @@ def main():
         del r["layer"]
         torch.cuda.empty_cache()
     if args.only in (None, "dense"):
+        # the 16 x 32 x 4096 GEMM (203 KB: launch-bound, its time is what is reported)
+        r0 = bench_dense(args.steps, args.warmup, name="dense_m16_n32_k4096")
+        result["dense_small"] = {"workload": "dense_m16_n32_k4096", "us": round(r0["ms"] * 1e3, 2),
+                                 "graph_us": round(r0["graph_ms"] * 1e3, 2)}
         r = bench_dense(args.steps, args.warmup)
         result["dense"] = {"workload": "dense_m64_n4096_k7168", "ms": round(r["ms"], 5),
                            "weight_GBps": round(r["gbs"], 1), "frac_hbm": round(r["gbs"] / PEAK_HBM_GBS, 4),
