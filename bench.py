@@ -51,7 +51,8 @@ TRAFFIC_SRC_SHA256 = "d1136d728a94c1ff832ba1fb8b3ab2b52fd2df32fe3da2d2b0a0a81969
 TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8802236000, "moe_decode_t8": 1008487008}
 
 
-GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "mx_codec.hpp")
+GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "mx_codec.hpp",
+                "fc2_combine.hip")
 
 
 def gemm_sources_sha256():
@@ -96,9 +97,10 @@ def moe_weights_dev(cfg):
 
 
 class Layer:
-    """Pre-allocated buffers of one MoE layer; step() = the four C-ABI calls."""
+    """Pre-allocated buffers of one MoE layer; step() = the four C-ABI calls, or with
+    fused=True (at most 64 tokens) three: FC2 and the combine in one call."""
 
-    def __init__(self, cfg, weights_sets, y_dtype=torch.bfloat16):
+    def __init__(self, cfg, weights_sets, y_dtype=torch.bfloat16, fused=False):
         self.cfg = cfg
         T, H, I, k = cfg["T"], cfg["H"], cfg["I"], cfg["k"]
         self.fmt = cfg["act_fmt"]
@@ -106,6 +108,7 @@ class Layer:
         self.logits = to_dev(dg.logits(cfg["seed"], T, cfg["E"], cfg["routing"]))
         self.sets = weights_sets
         self.y_dtype = y_dtype
+        self.fused = fused
         self.T, self.k = T, k
         R = T * k
         fp4 = self.fmt == "e2m1"
@@ -137,6 +140,15 @@ class Layer:
         ops._check(lib.moe_route_permute(P(self.logits), self.T, c["E"], self.k, P(self.ids), P(self.gates),
                                          P(self.offs), P(self.sp), P(self.pr), st), "route")
         if ev: ev[2].record()
+        if self.fused:
+            ops._check(lib.moe_grouped_mxfp4_gemm_combine(
+                P(self.q), P(self.qs), f, self.T, self.k, c["H"], c["I"], c["E"], P(self.offs), P(self.sp),
+                P(self.gates), P(w1), P(s1), P(w2), P(s2), P(self.h), P(self.hs), P(self.out), ops.MXF_BF16, st),
+                "grouped+combine")
+            if ev:
+                ev[3].record()
+                ev[4].record()
+            return
         ops._check(lib.moe_grouped_mxfp4_gemm(P(self.q), P(self.qs), f, self.T, self.k, c["H"], c["I"], c["E"],
                                               P(self.offs), P(self.sp), P(w1), P(s1), P(w2), P(s2), P(self.h),
                                               P(self.hs), P(self.y), ops.DTYPES[self.y_dtype], st), "grouped")
@@ -194,16 +206,19 @@ def time_graph_steps(layer, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def bench_moe(name, steps, warmup, rotate):
+def bench_moe(name, steps, warmup, rotate, fused=False, sets=None):
     cfg = dg.WORKLOADS[name]
-    log(f"[bench] {name}: generating inputs ...")
-    t0 = time.time()
-    base = moe_weights_dev(cfg)
-    sets = [base] + [tuple(t.clone() for t in base) for _ in range(rotate - 1)]
-    layer = Layer(cfg, sets)
-    log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s ({rotate} weight set(s))")
+    if sets is None:
+        log(f"[bench] {name}: generating inputs ...")
+        t0 = time.time()
+        base = moe_weights_dev(cfg)
+        sets = [base] + [tuple(t.clone() for t in base) for _ in range(rotate - 1)]
+        log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s ({rotate} weight set(s))")
+    layer = Layer(cfg, sets, fused=fused)
     wall, st = time_steps(layer.step, steps, warmup, nev=5)
     names = ["quantize", "route_permute", "grouped_gemm", "combine"]
+    if fused:
+        names = ["quantize", "route_permute", "grouped_gemm_combine"]
     stage_ms = {n: float(np.mean(st[:, j])) for j, n in enumerate(names)}
     offs = layer.offs.cpu().numpy()
     counts = np.diff(offs)
@@ -212,7 +227,7 @@ def bench_moe(name, steps, warmup, rotate):
     flops = pairs * FLOP_PER_PAIR
     wbytes = touched * BYTES_PER_EXPERT
     return dict(cfg=cfg, ms=wall * 1e3, stage_ms=stage_ms, touched=touched, pairs=pairs, flops=flops,
-                wbytes=wbytes, max_rows=int(counts.max()), layer=layer)
+                wbytes=wbytes, max_rows=int(counts.max()), layer=layer, sets=sets)
 
 
 def bench_dense(steps, warmup, rotate=48, name="dense_m64_n4096_k7168"):
@@ -446,21 +461,30 @@ def main():
         })
         if ceil:
             result["frac_of_measured_ceiling"] = round(g_tflops / ceil["mfma_e2m1_random_TFLOPs"], 4)
-        del r["layer"]
+        del r["layer"], r["sets"]
         torch.cuda.empty_cache()
     if args.only in (None, "decode"):
         name = "moe_decode_t8"
-        r = bench_moe(name, args.steps * 5, args.warmup, rotate=2)
-        g_ms = r["stage_ms"]["grouped_gemm"]
+        # the product's decode step: FC2 fused with the combine; the unfused four-call
+        # step on the same weights beside it
+        r = bench_moe(name, args.steps * 5, args.warmup, rotate=2, fused=True)
+        u = bench_moe(name, args.steps * 5, args.warmup, rotate=2, sets=r["sets"])
+        g_ms = r["stage_ms"]["grouped_gemm_combine"]
+        gbs = lambda ms: round(r["wbytes"] / (ms * 1e-3) / 1e9, 1)
         dec = {"workload": name, "ms_per_step": round(r["ms"], 4),
                "stages_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
                "touched_experts": r["touched"], "weight_bytes": r["wbytes"],
-               "weight_GBps_layer": round(r["wbytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-               "weight_GBps_grouped_gemm": round(r["wbytes"] / (g_ms * 1e-3) / 1e9, 1),
-               "roofline": {"kernel": "moe_grouped_mxfp4_gemm (FC1 + FC2 kernels)", "bound": "hbm",
-                            "achieved": round(r["wbytes"] / (g_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
-                            "unit": "GB/s", "frac": round(r["wbytes"] / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                            "traffic": measured_traffic(name)}}
+               "weight_GBps_layer": gbs(r["ms"]),
+               "weight_GBps_grouped_gemm_combine": gbs(g_ms),
+               "roofline": {"kernel": "moe_grouped_mxfp4_gemm_combine (FC1 + fused FC2/combine kernels)",
+                            "bound": "hbm", "achieved": gbs(g_ms), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(gbs(g_ms) / PEAK_HBM_GBS, 4),
+                            "traffic": measured_traffic(name + "_fused")}}
+        ug = u["stage_ms"]["grouped_gemm"]
+        dec["unfused"] = {"ms_per_step": round(u["ms"], 4),
+                          "stages_ms": {k: round(v, 4) for k, v in u["stage_ms"].items()},
+                          "weight_GBps_layer": gbs(u["ms"]), "weight_GBps_grouped_gemm": gbs(ug),
+                          "traffic_grouped_gemm": measured_traffic(name)}
         g_wall = time_graph_steps(r["layer"], args.steps * 5, args.warmup)
         if ceil:
             dec["frac_of_measured_ceiling"] = round(dec["roofline"]["achieved"] / ceil["hbm_read_GBps"], 4)
@@ -471,7 +495,7 @@ def main():
                            "dtype": "mxfp8 x mxfp4 (e4m3 x e2m1, fp32 accumulate)",
                            "config": {"workload": name}, "roofline": dec["roofline"]})
         result["decode"] = dec
-        del r["layer"]
+        del r["layer"], r["sets"], u["layer"], u["sets"]
         torch.cuda.empty_cache()
     if args.only in (None, "skewed"):
         name = "moe_prefill_t2048_zipf"
@@ -489,7 +513,7 @@ def main():
             sk["frac_of_measured_ceilings"] = {
                 "mfma": round(sk["grouped_TFLOPs"] / ceil["mfma_e4m3xe2m1_random_TFLOPs"], 4),
                 "hbm": round(sk["touched_weight_GBps_grouped"] / ceil["hbm_read_GBps"], 4)}
-        del r["layer"]
+        del r["layer"], r["sets"]
         torch.cuda.empty_cache()
     if args.only in (None, "dense"):
         # the 16 x 32 x 4096 GEMM (203 KB: launch-bound, its time is what is reported)

@@ -262,6 +262,36 @@ int moe_grouped_mxfp4_gemm(const uint8_t* q, const uint8_t* q_scale, int act_fmt
                            void* y, int y_dtype, mxf_stream stream);
 
 /*
+ * moe_grouped_mxfp4_gemm_combine - both expert FCs with FC2 fused into the
+ * gate-weighted combine, for decode-sized batches:
+ *   out[t] = sum_{j=0..topk-1} gates[t][j] * (h_hat[r(t,j)] . W2_hat[e(t,j)]^T)
+ * Defined by: the FC1 / SwiGLU / requantisation steps of moe_grouped_mxfp4_gemm
+ * above, then the combine half of MoE dispatch/combine (page "Domestic GPUs are
+ * awesome! ... DeepSeek-V4") applied inside the FC2 kernel, which the closing
+ * lessons of page "【DeepSeek V4】Triton FP4 优化实战" motivate (cut the data moved
+ * between steps, not the arithmetic). The FC2 products of one output column for
+ * every (token, slot) pair stay in fp32 on the chip (y is never stored and never
+ * rounded to bf16) and are summed in slot order j = 0, 1, ... with fused
+ * multiply-adds, then stored as out_dtype (bf16: round to nearest even).
+ *   q, q_scale, act_fmt, expert_offsets, sorted_pair, w1.., w2.., h, h_scale
+ *                  as for moe_grouped_mxfp4_gemm (h is still written: FC2 reads it)
+ *   gates          [T][topk] fp32, as written by moe_route_permute
+ *   out            [T][H] fp32 or bf16 (out_dtype), caller-allocated
+ * Requires T <= 64 (larger batches: moe_grouped_mxfp4_gemm + moe_unpermute_combine,
+ * else UNSUPPORTED) and the shape rules of moe_grouped_mxfp4_gemm. Deterministic:
+ * no atomics, fixed summation order. T == 0 is a no-op.
+ * Errors: NULL, SHAPE, ALIGN, FORMAT, UNSUPPORTED.
+ */
+int moe_grouped_mxfp4_gemm_combine(const uint8_t* q, const uint8_t* q_scale, int act_fmt,
+                                   int64_t T, int32_t topk, int64_t H, int64_t I, int32_t E,
+                                   const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                   const float* gates,
+                                   const uint8_t* w1, const uint8_t* w1_scale,
+                                   const uint8_t* w2, const uint8_t* w2_scale,
+                                   uint8_t* h, uint8_t* h_scale,
+                                   void* out, int out_dtype, mxf_stream stream);
+
+/*
  * moe_unpermute_combine - out[t] = sum_{j=0..topk-1} gates[t][j] * y[pair_row[t*topk+j]]
  * Defined by: the combine half of MoE dispatch/combine, page "Domestic GPUs are
  * awesome! ... DeepSeek-V4"; the gates are the routing weights of page "【DeepSeek

@@ -184,6 +184,29 @@ int moe_grouped_mxfp4_gemm(const uint8_t* q, const uint8_t* q_scale, int act_fmt
   return rc ? MXF_ERR_LAUNCH : MXF_OK;
 }
 
+int moe_grouped_mxfp4_gemm_combine(const uint8_t* q, const uint8_t* q_scale, int act_fmt, int64_t T, int32_t topk,
+                                   int64_t H, int64_t I, int32_t E, const int32_t* expert_offsets,
+                                   const int32_t* sorted_pair, const float* gates, const uint8_t* w1,
+                                   const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale, uint8_t* h,
+                                   uint8_t* h_scale, void* out, int out_dtype, mxf_stream stream) {
+  if (!valid_elem(act_fmt) || !valid_dtype(out_dtype)) return MXF_ERR_FORMAT;
+  if (T < 0 || topk < 1 || topk > 8 || E < 1 || topk > E) return MXF_ERR_SHAPE;
+  if (H <= 0 || H % 512 != 0 || I <= 0 || I % 512 != 0) return MXF_ERR_SHAPE;
+  if (E > 1024 || T > 64) return MXF_ERR_UNSUPPORTED;
+  if (2 * I * (H / 2) >= ((int64_t)1 << 32) || H * (I / 2) >= ((int64_t)1 << 32)) return MXF_ERR_UNSUPPORTED;
+  if (T == 0) return MXF_OK;
+  if (!q || !q_scale || !expert_offsets || !sorted_pair || !gates || !w1 || !w1_scale || !w2 || !w2_scale || !h ||
+      !h_scale || !out)
+    return MXF_ERR_NULL;
+  const void* ptrs[] = {q, q_scale, expert_offsets, sorted_pair, gates, w1, w1_scale, w2, w2_scale, h, h_scale, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MXF_ERR_ALIGN;
+  int rc = mxf::launch_grouped_gemm_combine(q, q_scale, act_fmt == MXF_E2M1, T, topk, H, I, E, expert_offsets,
+                                            sorted_pair, gates, w1, w1_scale, w2, w2_scale, h, h_scale, out,
+                                            out_dtype == MXF_BF16, as_stream(stream));
+  return rc ? MXF_ERR_LAUNCH : MXF_OK;
+}
+
 int moe_unpermute_combine(const void* y, int y_dtype, const float* gates, const int32_t* pair_row, int64_t T,
                           int32_t topk, int64_t H, void* out, int out_dtype, mxf_stream stream) {
   if (!valid_dtype(y_dtype) || !valid_dtype(out_dtype)) return MXF_ERR_FORMAT;

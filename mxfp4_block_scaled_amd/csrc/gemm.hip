@@ -114,4 +114,33 @@ int launch_grouped_gemm(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, 
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+int launch_grouped_gemm_combine(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, int64_t T, int topk,
+                                int64_t H, int64_t I, int E, const int32_t* expert_offsets,
+                                const int32_t* sorted_pair, const float* gates, const uint8_t* w1,
+                                const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale, uint8_t* h,
+                                uint8_t* h_scale, void* out, bool out_bf16, hipStream_t stream) {
+  if (T == 0) return 0;
+  if (T > 64) return -1;
+  GemmArgs f1{};
+  f1.act = q;
+  f1.act_rows = T;
+  f1.act_scale = q_scale;
+  f1.w = w1;
+  f1.w_scale = w1_scale;
+  f1.offsets = expert_offsets;
+  f1.sorted_pair = sorted_pair;
+  f1.h = h;
+  f1.h_scale = h_scale;
+  f1.K = H;
+  f1.N = 2 * I;
+  f1.I = I;
+  f1.topk = topk;
+  f1.E = E;
+  const int64_t R = T * topk, slots = R < E ? R : E;
+  launch_stream_gemm(kModeFC1, false, act_fp4, f1, (int)cdiv(T, 16), dim3((unsigned)(I / 32), (unsigned)slots),
+                     stream);
+  return launch_fc2_combine(h, h_scale, act_fp4, T, topk, H, I, E, expert_offsets, sorted_pair, gates, w2,
+                            w2_scale, out, out_bf16, stream);
+}
+
 }  // namespace mxf

@@ -51,4 +51,15 @@ int launch_grouped_gemm(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, 
                         const uint8_t* w2, const uint8_t* w2_scale, uint8_t* h, uint8_t* h_scale,
                         void* y, bool y_bf16, hipStream_t stream);
 
+// decode-sized batches (T <= 64): FC1 through the weight-streaming kernel, then FC2 fused
+// with the gate-weighted combine (fc2_combine.hip); -1 when T > 64
+int launch_grouped_gemm_combine(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, int64_t T, int topk,
+                                int64_t H, int64_t I, int E, const int32_t* expert_offsets,
+                                const int32_t* sorted_pair, const float* gates, const uint8_t* w1,
+                                const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale, uint8_t* h,
+                                uint8_t* h_scale, void* out, bool out_bf16, hipStream_t stream);
+int launch_fc2_combine(const uint8_t* h, const uint8_t* h_scale, bool act_fp4, int64_t T, int topk, int64_t H,
+                       int64_t I, int E, const int32_t* offsets, const int32_t* sorted_pair, const float* gates,
+                       const uint8_t* w2, const uint8_t* w2_scale, void* out, bool out_bf16, hipStream_t stream);
+
 }  // namespace mxf

@@ -39,6 +39,8 @@ SIGNATURES = {
     "moe_grouped_mxfp4_gemm": (_c_int, [_p, _p, _c_int, _c_i64, _c_i32, _c_i64, _c_i64, _c_i32,
                                         _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_int, _p]),
     "moe_unpermute_combine": (_c_int, [_p, _c_int, _p, _p, _c_i64, _c_i32, _c_i64, _p, _c_int, _p]),
+    "moe_grouped_mxfp4_gemm_combine": (_c_int, [_p, _p, _c_int, _c_i64, _c_i32, _c_i64, _c_i64, _c_i32, _p, _p,
+                                                _p, _p, _p, _p, _p, _p, _p, _p, _c_int, _p]),
     # include/mxf_ceilings.h: achievable-rate probes (measurement helpers)
     "mxf_ceiling_mfma_flops": (_c_i64, [_c_int]),
     "mxf_ceiling_mfma": (_c_int, [_c_int, _p, _c_i64, _c_int, _c_int, _p, _p]),
@@ -311,14 +313,63 @@ def moe_unpermute_combine(y, gates, pair_row, T, topk, out_dtype=torch.bfloat16,
     return out
 
 
+def moe_grouped_mxfp4_gemm_combine(q, q_scale, act_fmt, T, topk, expert_offsets, sorted_pair, gates, w1,
+                                   w1_scale, w2, w2_scale, out_dtype=torch.bfloat16, h=None, h_scale=None,
+                                   out=None):
+    """Both expert FCs with FC2 fused into the gate-weighted combine (T <= 64).
+    Returns (h, h_scale, out) with out [T][H]."""
+    dev = _dev(q)
+    for t in (q_scale, expert_offsets, sorted_pair, gates, w1, w1_scale, w2, w2_scale):
+        _dev(t)
+    if w1.dim() != 3:
+        raise RuntimeError("w1 must be [E][2I][H/2]")
+    E, twoI, Hh = w1.shape
+    I = twoI // 2
+    H = Hh * 2
+    f = FMTS[act_fmt]
+    R = T * topk
+    fp4 = f == MXF_E2M1
+    _need(q, "q", torch.uint8, (T, H // 2 if fp4 else H))
+    _need(q_scale, "q_scale", torch.uint8, (T, H // 32))
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    _need(sorted_pair, "sorted_pair", torch.int32, ((">=", R),))
+    _need(gates, "gates", torch.float32, (T, topk))
+    _need(w1, "w1", torch.uint8, (E, 2 * I, H // 2))
+    _need(w1_scale, "w1_scale", torch.uint8, (E, 2 * I, H // 32))
+    _need(w2, "w2", torch.uint8, (E, H, I // 2))
+    _need(w2_scale, "w2_scale", torch.uint8, (E, H, I // 32))
+    if h is None:
+        h = torch.empty((max(R, 1), I // 2 if fp4 else I), dtype=torch.uint8, device=dev)
+    if h_scale is None:
+        h_scale = torch.empty((max(R, 1), I // 32), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((max(T, 1), H), dtype=out_dtype, device=dev)
+    for t in (h, h_scale, out):
+        _dev(t)
+    _need(h, "h", torch.uint8, ((">=", R), I // 2 if fp4 else I))
+    _need(h_scale, "h_scale", torch.uint8, ((">=", R), I // 32))
+    _need(out, "out", (torch.float32, torch.bfloat16), ((">=", T), H))
+    _check(load().moe_grouped_mxfp4_gemm_combine(
+        _ptr(q), _ptr(q_scale), f, T, topk, H, I, E, _ptr(expert_offsets), _ptr(sorted_pair), _ptr(gates),
+        _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(h), _ptr(h_scale), _ptr(out),
+        DTYPES[out.dtype], _stream(dev)), "moe_grouped_mxfp4_gemm_combine")
+    return h[:R], h_scale[:R], out[:T]
+
+
 def moe_layer(x, logits, w1, w1_scale, w2, w2_scale, topk, act_fmt="e4m3", y_dtype=torch.bfloat16,
-              out_dtype=torch.bfloat16):
-    """The whole expert layer through the four C-ABI calls (one stream, no host sync)."""
+              out_dtype=torch.bfloat16, fused=False):
+    """The whole expert layer through the C-ABI calls (one stream, no host sync).
+    fused=True (T <= 64): FC2 and the combine in one kernel; y is not formed (None)."""
     T = x.shape[0]
     q, qs = mxfp4_quantize_act(x, act_fmt)
     ids, gates, offs, sp, pr = moe_route_permute(logits, topk)
-    h, hs, y = moe_grouped_mxfp4_gemm(q, qs, act_fmt, T, topk, offs, sp, w1, w1_scale, w2, w2_scale, y_dtype)
-    out = moe_unpermute_combine(y, gates, pr, T, topk, out_dtype)
+    if fused:
+        h, hs, out = moe_grouped_mxfp4_gemm_combine(q, qs, act_fmt, T, topk, offs, sp, gates, w1, w1_scale, w2,
+                                                    w2_scale, out_dtype)
+        y = None
+    else:
+        h, hs, y = moe_grouped_mxfp4_gemm(q, qs, act_fmt, T, topk, offs, sp, w1, w1_scale, w2, w2_scale, y_dtype)
+        out = moe_unpermute_combine(y, gates, pr, T, topk, out_dtype)
     return dict(q=q, q_scale=qs, topk_ids=ids, gates=gates, expert_offsets=offs, sorted_pair=sp, pair_row=pr,
                 h=h, h_scale=hs, y=y, out=out)
 

@@ -60,6 +60,7 @@ from .moe import (  # noqa: F401
     moe_layer,
     fc1_swiglu_rows,
     fc1_abs_terms,
+    group_max_terms,
     fc2_rows,
     combine,
     row_normalised_error,

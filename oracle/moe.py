@@ -184,6 +184,21 @@ def fc1_abs_terms(a_hat_rows, w1, w1_scale):
     return np.abs(a_hat_rows) @ np.abs(dequant_weights(w1, w1_scale)).T
 
 
+def group_max_terms(a_hat_rows, w_hat, group=8):
+    """B[r, n] = sum over the K / group groups of `group` consecutive k of
+    (max over the group of |a_hat[r, k]|) * (max over the group of |w_hat[n, k]|).
+
+    Not part of the layer's result. It bounds from above the sum over groups of the
+    largest |a_k w_k| in each group, which scales the error of a summation that
+    aligns every group's products to the group's largest one before adding them."""
+    a = np.abs(np.asarray(a_hat_rows, dtype=np.float64))
+    w = np.abs(np.asarray(w_hat, dtype=np.float64))
+    K = a.shape[1]
+    am = a.reshape(a.shape[0], K // group, group).max(axis=2)
+    wm = w.reshape(w.shape[0], K // group, group).max(axis=2)
+    return am @ wm.T
+
+
 def moe_layer(x_bf16, logits, w1, s1, w2, s2, k, act_fmt, rows=None, workers=1, abs_terms=False):
     """The whole expert layer, expert by expert, in fp64.
 
@@ -195,7 +210,8 @@ def moe_layer(x_bf16, logits, w1, s1, w2, s2, k, act_fmt, rows=None, workers=1, 
     all of whose k rows were computed (others are NaN).
     workers: experts are independent; with workers > 1 they are computed on that
     many threads (the same per-expert arithmetic, only run concurrently).
-    abs_terms: also return 'G_abs' = fc1_abs_terms of the computed rows.
+    abs_terms: also return 'G_abs' = fc1_abs_terms and 'G_gmax' = group_max_terms
+    (groups of 8 along H) of FC1 for the computed rows.
     """
     x_bf16 = np.asarray(x_bf16)
     T, H = x_bf16.shape
@@ -216,6 +232,7 @@ def moe_layer(x_bf16, logits, w1, s1, w2, s2, k, act_fmt, rows=None, workers=1, 
     h_scale = np.zeros((R, I // 32), dtype=np.uint8)
     y = np.full((R, H), np.nan)
     G_abs = np.full((R, 2 * I), np.nan) if abs_terms else None
+    G_gmax = np.full((R, 2 * I), np.nan) if abs_terms else None
 
     def one_expert(e):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
@@ -231,6 +248,7 @@ def moe_layer(x_bf16, logits, w1, s1, w2, s2, k, act_fmt, rows=None, workers=1, 
         y[r] = fc2_rows(hq, hs, act_fmt, w2[e], s2[e])
         if abs_terms:
             G_abs[r] = fc1_abs_terms(a_hat, w1[e], s1[e])
+            G_gmax[r] = group_max_terms(a_hat, dequant_weights(w1[e], s1[e]))
 
     if workers > 1:
         from concurrent.futures import ThreadPoolExecutor
@@ -250,7 +268,7 @@ def moe_layer(x_bf16, logits, w1, s1, w2, s2, k, act_fmt, rows=None, workers=1, 
         out[tk] = acc
     return dict(q=q, q_scale=q_scale, topk_ids=topk_ids, gates=gates,
                 expert_offsets=offsets, sorted_pair=sorted_pair, pair_row=pair_row,
-                G=G, G_abs=G_abs, h_pre=h_pre, h=h_codes, h_scale=h_scale, y=y, out=out,
+                G=G, G_abs=G_abs, G_gmax=G_gmax, h_pre=h_pre, h=h_codes, h_scale=h_scale, y=y, out=out,
                 computed_rows=want, computed_tokens=done)
 
 

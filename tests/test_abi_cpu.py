@@ -134,6 +134,33 @@ def test_grouped_gemm_errors():
     assert call(T=0, q=None) == OK
 
 
+def test_fused_fc2_combine_errors():
+    lib = _lib()
+
+    def call(**kw):
+        a = dict(q=A, qs=A, fmt=1, T=8, k=6, H=7168, I=2048, E=256, off=A, sp=A, g=A, w1=A, s1=A, w2=A, s2=A,
+                 h=A, hs=A, out=A, od=1)
+        a.update(kw)
+        return lib.moe_grouped_mxfp4_gemm_combine(
+            a["q"], a["qs"], a["fmt"], a["T"], a["k"], a["H"], a["I"], a["E"], a["off"], a["sp"], a["g"],
+            a["w1"], a["s1"], a["w2"], a["s2"], a["h"], a["hs"], a["out"], a["od"], None)
+
+    assert call(T=65) == UNSUPPORTED  # decode-sized batches only
+    assert call(H=7168 + 128) == SHAPE
+    assert call(I=2048 + 32) == SHAPE
+    assert call(k=9) == SHAPE
+    assert call(k=7, E=6) == SHAPE
+    assert call(fmt=5) == FORMAT
+    assert call(od=3) == FORMAT
+    assert call(E=4096) == UNSUPPORTED
+    assert call(H=1 << 20, I=4096) == UNSUPPORTED  # one expert's w1 above 4 GiB
+    assert call(g=None) == NULL
+    assert call(out=None) == NULL
+    assert call(g=U) == ALIGN
+    assert call(out=U) == ALIGN
+    assert call(T=0, q=None, g=None) == OK
+
+
 def test_combine_errors():
     lib = _lib()
     assert lib.moe_unpermute_combine(A, 1, A, A, 8, 6, 7164, A, 1, None) == SHAPE  # H % 8

@@ -80,6 +80,40 @@ def test_layer_outputs_stay_inside_their_buffers(T, H, I, E, k, fmt, routing, y_
     assert torch.isfinite(b["out"][-1].float()).all()
 
 
+@pytest.mark.parametrize("T,H,I,E,k,fmt,out_dtype", [
+    (8, 1024, 512, 16, 6, "e4m3", torch.bfloat16),   # decode-shaped
+    (61, 1024, 1536, 4, 2, "e2m1", torch.float32),   # ~30 rows per expert, 3 super-steps
+    (64, 512, 512, 300, 8, "e4m3", torch.float32),   # T * topk = 512, more than 256 experts
+])
+def test_fused_fc2_combine_outputs_stay_inside_their_buffers(T, H, I, E, k, fmt, out_dtype):
+    lib = ops.load()
+    st = ops._stream(torch.device("cuda"))
+    x = bf16_dev(dg.activations(53, T, H))
+    logits = torch.from_numpy(dg.logits(53, T, E, "normal")).cuda()
+    w1, s1, w2, s2 = [torch.from_numpy(np.ascontiguousarray(t)).cuda() for t in dg.moe_weights(53, E, H, I, 120, 128)]
+    fp4 = fmt == "e2m1"
+    f = ops.FMTS[fmt]
+    R = T * k
+    bufs = {
+        "q": Guarded((T, H // 2 if fp4 else H), torch.uint8, 31), "q_scale": Guarded((T, H // 32), torch.uint8, 32),
+        "ids": Guarded((T, k), torch.int32, 33), "gates": Guarded((T, k), torch.float32, 34),
+        "offs": Guarded((E + 1,), torch.int32, 35), "sp": Guarded((R,), torch.int32, 36),
+        "pr": Guarded((R,), torch.int32, 37), "h": Guarded((R, I // 2 if fp4 else I), torch.uint8, 38),
+        "hs": Guarded((R, I // 32), torch.uint8, 39), "out": Guarded((T, H), out_dtype, 40),
+    }
+    b = {n: v.t for n, v in bufs.items()}
+    ops._check(lib.mxfp4_quantize_act(_p(x), ops.MXF_BF16, T, H, f, _p(b["q"]), _p(b["q_scale"]), st), "quantize")
+    ops._check(lib.moe_route_permute(_p(logits), T, E, k, _p(b["ids"]), _p(b["gates"]), _p(b["offs"]), _p(b["sp"]),
+                                     _p(b["pr"]), st), "route")
+    ops._check(lib.moe_grouped_mxfp4_gemm_combine(
+        _p(b["q"]), _p(b["q_scale"]), f, T, k, H, I, E, _p(b["offs"]), _p(b["sp"]), _p(b["gates"]), _p(w1), _p(s1),
+        _p(w2), _p(s2), _p(b["h"]), _p(b["hs"]), _p(b["out"]), ops.DTYPES[out_dtype], st), "grouped+combine")
+    torch.cuda.synchronize()
+    for name, v in bufs.items():
+        v.check(name)
+    assert torch.isfinite(b["out"].float()).all()
+
+
 @pytest.mark.parametrize("M,N,K,fmt", [
     (37, 48, 5120, "e2m1"),   # M <= 64: K slices summed through the workspace
     (64, 4096, 7168, "e4m3"),  # the dense 64 x 4096 x 7168 shape

@@ -80,7 +80,7 @@ def _run_and_check(name, unit, stream_max):
     for key in ("q", "q_scale", "topk_ids", "expert_offsets", "sorted_pair", "pair_row"):
         assert np.array_equal(g[key], ref[key]), key
     I = ref["h_pre"].shape[1]
-    dh = h_error_bound(ref["G"][rows], ref["G_abs"][rows], I, fmt)
+    dh = h_error_bound(ref["G"][rows], ref["G_abs"][rows], I, fmt, ref["G_gmax"][rows])
     n_code, n_scale = straddle_check_bound(unpack_codes(g["h"], fmt), g["h_scale"], ref["h_pre"][rows], dh, fmt)
     # y, stage-isolated: the oracle's FC2 on the GPU's own h
     e_of_row = np.searchsorted(offs, rows, side="right") - 1

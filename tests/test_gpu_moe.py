@@ -38,7 +38,7 @@ def _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt, rows=None, tokens=None):
     rows = np.arange(T * k) if rows is None else np.asarray(rows)
     # h: the GPU's codes against the oracle's exact values within the error bound
     I = ref["h_pre"].shape[1]
-    dh = h_error_bound(ref["G"][rows], ref["G_abs"][rows], I, fmt)
+    dh = h_error_bound(ref["G"][rows], ref["G_abs"][rows], I, fmt, ref["G_gmax"][rows])
     straddle_check_bound(unpack_codes(g["h"][rows], fmt), g["h_scale"][rows], ref["h_pre"][rows], dh, fmt)
     # y: stage-isolated (oracle FC2 on the GPU's own h)
     e_of_row = np.searchsorted(ref["expert_offsets"], rows, side="right") - 1

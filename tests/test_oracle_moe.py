@@ -202,3 +202,20 @@ def test_threaded_layer_equals_serial_and_abs_terms_brute_force():
     pos = oracle.fc1_abs_terms(np.abs(q_hat[:2]), np.full((3, H // 2), 0x22, np.uint8),
                                np.full((3, H // 32), 127, np.uint8))
     assert np.allclose(pos, np.abs(q_hat[:2]).sum(1)[:, None], rtol=1e-15)
+
+
+def test_group_max_terms_against_loops():
+    """group_max_terms against plain loops over rows, columns and groups, and the
+    property it exists for: it bounds the sum over groups of the largest |a_k w_k|."""
+    rng = np.random.default_rng(31)
+    a = rng.standard_normal((3, 48)) * np.exp2(rng.integers(-8, 8, (3, 48)))
+    w = rng.standard_normal((5, 48))
+    B = oracle.group_max_terms(a, w)
+    for r in range(3):
+        for n in range(5):
+            want = sum(max(abs(a[r, k]) for k in range(g, g + 8)) * max(abs(w[n, k]) for k in range(g, g + 8))
+                       for g in range(0, 48, 8))
+            assert math.isclose(B[r, n], want, rel_tol=1e-12)
+            top = sum(max(abs(a[r, k] * w[n, k]) for k in range(g, g + 8)) for g in range(0, 48, 8))
+            assert top <= B[r, n] * (1 + 1e-12)
+    assert np.array_equal(oracle.group_max_terms(a, w, group=48), np.abs(a).max(1)[:, None] * np.abs(w).max(1)[None])

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.helpers import MFMA_RESIDUAL, h_error_bound, straddle_check_bound
+from tests.helpers import MFMA_RESIDUAL, MFMA_WINDOW, h_error_bound, straddle_check_bound
 
 
 def _block(seed):
@@ -111,10 +111,12 @@ def test_h_error_bound_covers_perturbed_accumulators(fmt):
     G = np.concatenate([g.standard_normal((50, I)) * 8, g.standard_normal((50, I)) * 8], axis=1)
     G[0, :8] = [-40, -10, -1.28, 0.0, 1e-9, 2.4, 12, 35]  # silu's minimum near -1.28, its flat tails
     G_abs = np.abs(G) * 60 + 1.0
-    dh = h_error_bound(G, G_abs, I, fmt)
+    G_gmax = G_abs / 5
+    dh = h_error_bound(G, G_abs, I, fmt, G_gmax)
     gg, uu = G[:, :I], G[:, I:]
     h = gg / (1 + np.exp(-gg)) * uu
-    dg, du = MFMA_RESIDUAL[fmt] * G_abs[:, :I], MFMA_RESIDUAL[fmt] * G_abs[:, I:]
+    d = MFMA_RESIDUAL[fmt] * G_abs + MFMA_WINDOW[fmt] * G_gmax
+    dg, du = d[:, :I], d[:, I:]
     for sg, su in [(1, 1), (1, -1), (-1, 1), (-1, -1)] + [tuple(g.uniform(-1, 1, 2)) for _ in range(20)]:
         g2, u2 = gg + sg * dg, uu + su * du
         h2 = g2 / (1 + np.exp(-g2)) * u2
