@@ -98,7 +98,8 @@ def moe_weights_dev(cfg):
 
 class Layer:
     """Pre-allocated buffers of one MoE layer; step() = the four C-ABI calls, or with
-    fused=True (at most 64 tokens) three: FC2 and the combine in one call."""
+    fused=True (at most 64 tokens) two: quantisation with routing, and both FCs with
+    FC2 fused into the combine."""
 
     def __init__(self, cfg, weights_sets, y_dtype=torch.bfloat16, fused=False):
         self.cfg = cfg
@@ -134,16 +135,24 @@ class Layer:
         self.i += 1
         f = ops.FMTS[self.fmt]
         if ev: ev[0].record()
-        ops._check(lib.mxfp4_quantize_act(P(self.x), ops.MXF_BF16, self.T, c["H"], f, P(self.q), P(self.qs), st),
-                   "quantize")
-        if ev: ev[1].record()
-        ops._check(lib.moe_route_permute(P(self.logits), self.T, c["E"], self.k, P(self.ids), P(self.gates),
-                                         P(self.offs), P(self.sp), P(self.pr), st), "route")
-        if ev: ev[2].record()
+        if self.fused:
+            ops._check(lib.moe_quantize_route(P(self.x), ops.MXF_BF16, P(self.logits), self.T, c["H"], c["E"],
+                                              self.k, f, P(self.q), P(self.qs), P(self.ids), P(self.gates),
+                                              P(self.offs), P(self.sp), P(self.pr), st), "quantize+route")
+            if ev:
+                ev[1].record()
+                ev[2].record()
+        else:
+            ops._check(lib.mxfp4_quantize_act(P(self.x), ops.MXF_BF16, self.T, c["H"], f, P(self.q), P(self.qs),
+                                              st), "quantize")
+            if ev: ev[1].record()
+            ops._check(lib.moe_route_permute(P(self.logits), self.T, c["E"], self.k, P(self.ids), P(self.gates),
+                                             P(self.offs), P(self.sp), P(self.pr), st), "route")
+            if ev: ev[2].record()
         if self.fused:
             ops._check(lib.moe_grouped_mxfp4_gemm_combine(
                 P(self.q), P(self.qs), f, self.T, self.k, c["H"], c["I"], c["E"], P(self.offs), P(self.sp),
-                P(self.gates), P(w1), P(s1), P(w2), P(s2), P(self.h), P(self.hs), P(self.out), ops.MXF_BF16, st),
+                P(self.ids), P(self.pr), P(self.gates), P(w1), P(s1), P(w2), P(s2), P(self.h), P(self.hs), P(self.out), ops.MXF_BF16, st),
                 "grouped+combine")
             if ev:
                 ev[3].record()
@@ -215,11 +224,14 @@ def bench_moe(name, steps, warmup, rotate, fused=False, sets=None):
         sets = [base] + [tuple(t.clone() for t in base) for _ in range(rotate - 1)]
         log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s ({rotate} weight set(s))")
     layer = Layer(cfg, sets, fused=fused)
-    wall, st = time_steps(layer.step, steps, warmup, nev=5)
+    # the step's wall time from a loop without timing events (their markers add gaps
+    # between kernels), then the per-stage times from a second loop with events
+    wall, _ = time_steps(layer.step, steps, warmup)
+    _, st = time_steps(layer.step, steps, 1, nev=5)
     names = ["quantize", "route_permute", "grouped_gemm", "combine"]
     if fused:
-        names = ["quantize", "route_permute", "grouped_gemm_combine"]
-    stage_ms = {n: float(np.mean(st[:, j])) for j, n in enumerate(names)}
+        names = ["quantize_route", None, "grouped_gemm_combine"]  # one launch for the first two
+    stage_ms = {n: float(np.mean(st[:, j])) for j, n in enumerate(names) if n}
     offs = layer.offs.cpu().numpy()
     counts = np.diff(offs)
     touched = int((counts > 0).sum())

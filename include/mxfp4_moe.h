@@ -231,6 +231,24 @@ int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t topk,
                       int32_t* sorted_pair, int32_t* pair_row, mxf_stream stream);
 
 /*
+ * moe_quantize_route - mxfp4_quantize_act of the layer input and moe_route_permute
+ * of its router logits in one launch, for decode-sized batches.
+ * Defined by: the two calls above (the same steps, outputs bit-identical to them);
+ * the two steps share no data, so one launch replaces two (at decode sizes a
+ * launch's fixed cost is most of either step's time).
+ *   x [T][H] bf16 or fp32 (x_dtype); logits [T][E] fp32
+ *   q, q_scale     [T][H] (E4M3) or [T][H/2] (E2M1), [T][H/32], as mxfp4_quantize_act
+ *   topk_ids, gates, expert_offsets, sorted_pair, pair_row   as moe_route_permute
+ * Requires T <= 64 and E <= 256 (else UNSUPPORTED: use the two calls), H % 32 == 0,
+ * 1 <= topk <= min(E, 8). expert_offsets is written (all zero) even when T == 0.
+ * Errors: NULL, SHAPE, ALIGN, FORMAT, UNSUPPORTED.
+ */
+int moe_quantize_route(const void* x, int x_dtype, const float* logits, int64_t T, int64_t H,
+                       int32_t E, int32_t topk, int act_fmt, uint8_t* q, uint8_t* q_scale,
+                       int32_t* topk_ids, float* gates, int32_t* expert_offsets,
+                       int32_t* sorted_pair, int32_t* pair_row, mxf_stream stream);
+
+/*
  * moe_grouped_mxfp4_gemm - both expert FCs for every (token, expert) pair.
  * Defined by: page "DGX Spark 原生 FP4 矩阵指令" section 二 (the MoE MXFP4 entry;
  * weights stay FP4 into the matrix instruction), page "【DeepSeek V4】Triton FP4
@@ -275,7 +293,9 @@ int moe_grouped_mxfp4_gemm(const uint8_t* q, const uint8_t* q_scale, int act_fmt
  * multiply-adds, then stored as out_dtype (bf16: round to nearest even).
  *   q, q_scale, act_fmt, expert_offsets, sorted_pair, w1.., w2.., h, h_scale
  *                  as for moe_grouped_mxfp4_gemm (h is still written: FC2 reads it)
- *   gates          [T][topk] fp32, as written by moe_route_permute
+ *   topk_ids, pair_row, gates   [T][topk] int32, [T*topk] int32, [T][topk] fp32,
+ *                  as written by moe_route_permute (FC1 reads the expert-grouped
+ *                  order, the fused FC2 the token-major one)
  *   out            [T][H] fp32 or bf16 (out_dtype), caller-allocated
  * Requires T <= 64 (larger batches: moe_grouped_mxfp4_gemm + moe_unpermute_combine,
  * else UNSUPPORTED) and the shape rules of moe_grouped_mxfp4_gemm. Deterministic:
@@ -285,6 +305,7 @@ int moe_grouped_mxfp4_gemm(const uint8_t* q, const uint8_t* q_scale, int act_fmt
 int moe_grouped_mxfp4_gemm_combine(const uint8_t* q, const uint8_t* q_scale, int act_fmt,
                                    int64_t T, int32_t topk, int64_t H, int64_t I, int32_t E,
                                    const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                   const int32_t* topk_ids, const int32_t* pair_row,
                                    const float* gates,
                                    const uint8_t* w1, const uint8_t* w1_scale,
                                    const uint8_t* w2, const uint8_t* w2_scale,

@@ -157,6 +157,26 @@ int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t topk, i
   return rc ? MXF_ERR_LAUNCH : MXF_OK;
 }
 
+int moe_quantize_route(const void* x, int x_dtype, const float* logits, int64_t T, int64_t H, int32_t E,
+                       int32_t topk, int act_fmt, uint8_t* q, uint8_t* q_scale, int32_t* topk_ids, float* gates,
+                       int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_row, mxf_stream stream) {
+  if (!valid_dtype(x_dtype) || !valid_elem(act_fmt)) return MXF_ERR_FORMAT;
+  if (T < 0 || H <= 0 || H % 32 != 0 || E < 1 || topk < 1 || topk > 8 || topk > E) return MXF_ERR_SHAPE;
+  if (!mxf::quantize_route_supported(T, E)) return MXF_ERR_UNSUPPORTED;
+  if (!expert_offsets) return MXF_ERR_NULL;
+  if (T > 0 && (!x || !logits || !q || !q_scale || !topk_ids || !gates || !sorted_pair || !pair_row))
+    return MXF_ERR_NULL;
+  if (!aligned16(expert_offsets)) return MXF_ERR_ALIGN;
+  if (T > 0) {
+    const void* ptrs[] = {x, logits, q, q_scale, topk_ids, gates, sorted_pair, pair_row};
+    for (const void* p : ptrs)
+      if (!aligned16(p)) return MXF_ERR_ALIGN;
+  }
+  int rc = mxf::launch_quantize_route(x, x_dtype == MXF_F32, H, act_fmt == MXF_E2M1, q, q_scale, logits, T, E, topk,
+                                      topk_ids, gates, expert_offsets, sorted_pair, pair_row, as_stream(stream));
+  return rc ? MXF_ERR_LAUNCH : MXF_OK;
+}
+
 int moe_grouped_mxfp4_gemm(const uint8_t* q, const uint8_t* q_scale, int act_fmt, int64_t T, int32_t topk,
                            int64_t H, int64_t I, int32_t E, const int32_t* expert_offsets,
                            const int32_t* sorted_pair, const uint8_t* w1, const uint8_t* w1_scale,
@@ -186,7 +206,8 @@ int moe_grouped_mxfp4_gemm(const uint8_t* q, const uint8_t* q_scale, int act_fmt
 
 int moe_grouped_mxfp4_gemm_combine(const uint8_t* q, const uint8_t* q_scale, int act_fmt, int64_t T, int32_t topk,
                                    int64_t H, int64_t I, int32_t E, const int32_t* expert_offsets,
-                                   const int32_t* sorted_pair, const float* gates, const uint8_t* w1,
+                                   const int32_t* sorted_pair, const int32_t* topk_ids, const int32_t* pair_row,
+                                   const float* gates, const uint8_t* w1,
                                    const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale, uint8_t* h,
                                    uint8_t* h_scale, void* out, int out_dtype, mxf_stream stream) {
   if (!valid_elem(act_fmt) || !valid_dtype(out_dtype)) return MXF_ERR_FORMAT;
@@ -195,14 +216,16 @@ int moe_grouped_mxfp4_gemm_combine(const uint8_t* q, const uint8_t* q_scale, int
   if (E > 1024 || T > 64) return MXF_ERR_UNSUPPORTED;
   if (2 * I * (H / 2) >= ((int64_t)1 << 32) || H * (I / 2) >= ((int64_t)1 << 32)) return MXF_ERR_UNSUPPORTED;
   if (T == 0) return MXF_OK;
-  if (!q || !q_scale || !expert_offsets || !sorted_pair || !gates || !w1 || !w1_scale || !w2 || !w2_scale || !h ||
-      !h_scale || !out)
+  if (!q || !q_scale || !expert_offsets || !sorted_pair || !topk_ids || !pair_row || !gates || !w1 || !w1_scale ||
+      !w2 || !w2_scale || !h || !h_scale || !out)
     return MXF_ERR_NULL;
-  const void* ptrs[] = {q, q_scale, expert_offsets, sorted_pair, gates, w1, w1_scale, w2, w2_scale, h, h_scale, out};
+  const void* ptrs[] = {q,  q_scale,  expert_offsets, sorted_pair, topk_ids, pair_row, gates,
+                        w1, w1_scale, w2,             w2_scale,    h,        h_scale,  out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return MXF_ERR_ALIGN;
   int rc = mxf::launch_grouped_gemm_combine(q, q_scale, act_fmt == MXF_E2M1, T, topk, H, I, E, expert_offsets,
-                                            sorted_pair, gates, w1, w1_scale, w2, w2_scale, h, h_scale, out,
+                                            sorted_pair, topk_ids, pair_row, gates, w1, w1_scale, w2, w2_scale, h,
+                                            h_scale, out,
                                             out_dtype == MXF_BF16, as_stream(stream));
   return rc ? MXF_ERR_LAUNCH : MXF_OK;
 }

@@ -116,7 +116,8 @@ int launch_grouped_gemm(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, 
 
 int launch_grouped_gemm_combine(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, int64_t T, int topk,
                                 int64_t H, int64_t I, int E, const int32_t* expert_offsets,
-                                const int32_t* sorted_pair, const float* gates, const uint8_t* w1,
+                                const int32_t* sorted_pair, const int32_t* topk_ids, const int32_t* pair_row,
+                                const float* gates, const uint8_t* w1,
                                 const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale, uint8_t* h,
                                 uint8_t* h_scale, void* out, bool out_bf16, hipStream_t stream) {
   if (T == 0) return 0;
@@ -139,8 +140,8 @@ int launch_grouped_gemm_combine(const uint8_t* q, const uint8_t* q_scale, bool a
   const int64_t R = T * topk, slots = R < E ? R : E;
   launch_stream_gemm(kModeFC1, false, act_fp4, f1, (int)cdiv(T, 16), dim3((unsigned)(I / 32), (unsigned)slots),
                      stream);
-  return launch_fc2_combine(h, h_scale, act_fp4, T, topk, H, I, E, expert_offsets, sorted_pair, gates, w2,
-                            w2_scale, out, out_bf16, stream);
+  return launch_fc2_combine(h, h_scale, act_fp4, T, topk, H, I, topk_ids, pair_row, gates, w2, w2_scale, out,
+                            out_bf16, stream);
 }
 
 }  // namespace mxf

@@ -14,6 +14,11 @@ int launch_quantize_act(const void* x, bool f32_in, int64_t rows, int64_t K, boo
 
 // routing: returns 1 if the sizes are outside what the kernels handle (nothing launched)
 int route_permute_supported(int64_t T, int E, int topk);
+// quantisation and routing in one launch for T <= 64 tokens and E <= 256 experts (route.hip)
+int quantize_route_supported(int64_t T, int E);
+int launch_quantize_route(const void* x, bool f32_in, int64_t H, bool fp4, uint8_t* q, uint8_t* q_scale,
+                          const float* logits, int64_t T, int E, int topk, int32_t* topk_ids, float* gates,
+                          int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_row, hipStream_t stream);
 int launch_route_permute(const float* logits, int64_t T, int E, int topk, int32_t* topk_ids,
                          float* gates, int32_t* expert_offsets, int32_t* sorted_pair,
                          int32_t* pair_row, hipStream_t stream);
@@ -55,11 +60,12 @@ int launch_grouped_gemm(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, 
 // with the gate-weighted combine (fc2_combine.hip); -1 when T > 64
 int launch_grouped_gemm_combine(const uint8_t* q, const uint8_t* q_scale, bool act_fp4, int64_t T, int topk,
                                 int64_t H, int64_t I, int E, const int32_t* expert_offsets,
-                                const int32_t* sorted_pair, const float* gates, const uint8_t* w1,
+                                const int32_t* sorted_pair, const int32_t* topk_ids, const int32_t* pair_row,
+                                const float* gates, const uint8_t* w1,
                                 const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale, uint8_t* h,
                                 uint8_t* h_scale, void* out, bool out_bf16, hipStream_t stream);
 int launch_fc2_combine(const uint8_t* h, const uint8_t* h_scale, bool act_fp4, int64_t T, int topk, int64_t H,
-                       int64_t I, int E, const int32_t* offsets, const int32_t* sorted_pair, const float* gates,
+                       int64_t I, const int32_t* topk_ids, const int32_t* pair_row, const float* gates,
                        const uint8_t* w2, const uint8_t* w2_scale, void* out, bool out_bf16, hipStream_t stream);
 
 }  // namespace mxf

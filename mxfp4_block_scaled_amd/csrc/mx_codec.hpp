@@ -112,4 +112,44 @@ __device__ __forceinline__ uint32_t quantize_block32(const float (&v)[32], uint3
   return byte;
 }
 
+// One 32-element block b of the activations (bf16 or fp32): codes and scale byte.
+template <bool kF32In, bool kFP4>
+__device__ __forceinline__ void quantize_act_block(const void* __restrict__ x, int64_t b, uint8_t* __restrict__ q,
+                                                   uint8_t* __restrict__ q_scale) {
+  float v[32];
+  if (kF32In) {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(x) + b * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float4 f = src[i];
+      v[4 * i + 0] = f.x;
+      v[4 * i + 1] = f.y;
+      v[4 * i + 2] = f.z;
+      v[4 * i + 3] = f.w;
+    }
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + b * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 w = src[i];
+      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j + 0] = __uint_as_float(ws[j] << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+      }
+    }
+  }
+  uint32_t out[8];
+  const uint32_t byte = quantize_block32<kFP4>(v, out);
+  if (kFP4) {
+    *reinterpret_cast<uint4*>(q + b * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+  } else {
+    uint4* dst = reinterpret_cast<uint4*>(q + b * 32);
+    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  }
+  q_scale[b] = (uint8_t)byte;
+}
+
 }  // namespace mxf

@@ -20,6 +20,7 @@
 // scratch) until the last launch overwrites it with the result, so the call
 // needs no workspace: this requires (nblocks + 1) * E <= T * k.
 #include "launch.hpp"
+#include "mx_codec.hpp"
 
 namespace mxf {
 
@@ -209,10 +210,11 @@ __global__ void __launch_bounds__(kSmallThreads) route_small_kernel(
 // mask per expert
 constexpr int kTinyT = 64, kTinyE = 256, kTinyThreads = 256;
 
-__global__ void __launch_bounds__(kTinyThreads) route_tiny_kernel(
-    const float* __restrict__ logits, int T, int E, int topk, int32_t* __restrict__ topk_ids,
-    float* __restrict__ gates, int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_pair,
-    int32_t* __restrict__ pair_row) {
+// the whole routing of T <= 64 tokens over E <= 256 experts by one workgroup of kTinyThreads
+__device__ __forceinline__ void route_tiny_body(const float* __restrict__ logits, int T, int E, int topk,
+                                                int32_t* __restrict__ topk_ids, float* __restrict__ gates,
+                                                int32_t* __restrict__ expert_offsets,
+                                                int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_row) {
   constexpr int L = 16, TPW = 64 / L, NW = kTinyThreads / 64;
   __shared__ unsigned long long bits[kTinyE];  // bit t: token t chose expert e
   __shared__ int sids[kTinyT * 8];
@@ -259,6 +261,63 @@ __global__ void __launch_bounds__(kTinyThreads) route_tiny_kernel(
       sorted_pair[r] = p;
     }
   }
+}
+
+__global__ void __launch_bounds__(kTinyThreads) route_tiny_kernel(
+    const float* __restrict__ logits, int T, int E, int topk, int32_t* __restrict__ topk_ids,
+    float* __restrict__ gates, int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ pair_row) {
+  route_tiny_body(logits, T, E, topk, topk_ids, gates, expert_offsets, sorted_pair, pair_row);
+}
+
+// Quantisation of the layer input and the routing in one launch (T <= 64, E <= 256):
+// workgroup 0 routes, workgroups 1.. quantise 256 blocks of 32 elements each. The two
+// steps share no data; one launch instead of two saves a launch's fixed cost, which
+// at decode sizes is most of either step's time.
+template <bool kF32In, bool kFP4>
+__global__ void __launch_bounds__(kTinyThreads) quantize_route_kernel(
+    const void* __restrict__ x, int64_t nblocks, uint8_t* __restrict__ q, uint8_t* __restrict__ q_scale,
+    const float* __restrict__ logits, int T, int E, int topk, int32_t* __restrict__ topk_ids,
+    float* __restrict__ gates, int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ pair_row) {
+  static_assert(kTinyThreads == 256, "one quantisation block per thread, 256 per workgroup");
+  if (blockIdx.x == 0) {
+    route_tiny_body(logits, T, E, topk, topk_ids, gates, expert_offsets, sorted_pair, pair_row);
+    return;
+  }
+  const int64_t b = (int64_t)(blockIdx.x - 1) * 256 + threadIdx.x;
+  if (b < nblocks) quantize_act_block<kF32In, kFP4>(x, b, q, q_scale);
+}
+
+int quantize_route_supported(int64_t T, int E) { return T >= 0 && T <= kTinyT && E >= 1 && E <= kTinyE; }
+
+int launch_quantize_route(const void* x, bool f32_in, int64_t H, bool fp4, uint8_t* q, uint8_t* q_scale,
+                          const float* logits, int64_t T, int E, int topk, int32_t* topk_ids, float* gates,
+                          int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_row, hipStream_t stream) {
+  if (!quantize_route_supported(T, E)) return -1;
+  const int64_t nblocks = T * (H / 32);
+  const dim3 grid((unsigned)(1 + cdiv(nblocks, 256))), block(kTinyThreads);
+  const int t = (int)T;
+  if (f32_in) {
+    if (fp4)
+      quantize_route_kernel<true, true><<<grid, block, 0, stream>>>(x, nblocks, q, q_scale, logits, t, E, topk,
+                                                                    topk_ids, gates, expert_offsets, sorted_pair,
+                                                                    pair_row);
+    else
+      quantize_route_kernel<true, false><<<grid, block, 0, stream>>>(x, nblocks, q, q_scale, logits, t, E, topk,
+                                                                     topk_ids, gates, expert_offsets, sorted_pair,
+                                                                     pair_row);
+  } else {
+    if (fp4)
+      quantize_route_kernel<false, true><<<grid, block, 0, stream>>>(x, nblocks, q, q_scale, logits, t, E, topk,
+                                                                     topk_ids, gates, expert_offsets, sorted_pair,
+                                                                     pair_row);
+    else
+      quantize_route_kernel<false, false><<<grid, block, 0, stream>>>(x, nblocks, q, q_scale, logits, t, E, topk,
+                                                                      topk_ids, gates, expert_offsets, sorted_pair,
+                                                                      pair_row);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // large T, launch 1: top-k, one token per group of L lanes (64 / L tokens per wave)

@@ -39,8 +39,10 @@ SIGNATURES = {
     "moe_grouped_mxfp4_gemm": (_c_int, [_p, _p, _c_int, _c_i64, _c_i32, _c_i64, _c_i64, _c_i32,
                                         _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_int, _p]),
     "moe_unpermute_combine": (_c_int, [_p, _c_int, _p, _p, _c_i64, _c_i32, _c_i64, _p, _c_int, _p]),
+    "moe_quantize_route": (_c_int, [_p, _c_int, _p, _c_i64, _c_i64, _c_i32, _c_i32, _c_int, _p, _p, _p, _p, _p, _p,
+                                    _p, _p]),
     "moe_grouped_mxfp4_gemm_combine": (_c_int, [_p, _p, _c_int, _c_i64, _c_i32, _c_i64, _c_i64, _c_i32, _p, _p,
-                                                _p, _p, _p, _p, _p, _p, _p, _p, _c_int, _p]),
+                                                _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_int, _p]),
     # include/mxf_ceilings.h: achievable-rate probes (measurement helpers)
     "mxf_ceiling_mfma_flops": (_c_i64, [_c_int]),
     "mxf_ceiling_mfma": (_c_int, [_c_int, _p, _c_i64, _c_int, _c_int, _p, _p]),
@@ -313,13 +315,40 @@ def moe_unpermute_combine(y, gates, pair_row, T, topk, out_dtype=torch.bfloat16,
     return out
 
 
-def moe_grouped_mxfp4_gemm_combine(q, q_scale, act_fmt, T, topk, expert_offsets, sorted_pair, gates, w1,
-                                   w1_scale, w2, w2_scale, out_dtype=torch.bfloat16, h=None, h_scale=None,
-                                   out=None):
+def moe_quantize_route(x, logits, topk, act_fmt="e4m3"):
+    """mxfp4_quantize_act(x) and moe_route_permute(logits) in one launch (T <= 64,
+    E <= 256). Returns (q, q_scale, topk_ids, gates, expert_offsets, sorted_pair, pair_row)."""
+    dev = _dev(x)
+    _dev(logits)
+    if x.dim() != 2 or logits.dim() != 2:
+        raise RuntimeError("x must be [T][H] and logits [T][E]")
+    T, H = x.shape
+    E = logits.shape[1]
+    _need(x, "x", (torch.bfloat16, torch.float32), (T, H))
+    _need(logits, "logits", torch.float32, (T, E))
+    f = FMTS[act_fmt]
+    fp4 = f == MXF_E2M1
+    R = T * topk
+    q = torch.empty((T, H // 2 if fp4 else H), dtype=torch.uint8, device=dev)
+    qs = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+    ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    sp = torch.empty((max(R, 1),), dtype=torch.int32, device=dev)
+    pr = torch.empty((max(R, 1),), dtype=torch.int32, device=dev)
+    _check(load().moe_quantize_route(_ptr(x), DTYPES[x.dtype], _ptr(logits), T, H, E, topk, f, _ptr(q), _ptr(qs),
+                                     _ptr(ids), _ptr(gates), _ptr(offs), _ptr(sp), _ptr(pr), _stream(dev)),
+           "moe_quantize_route")
+    return q, qs, ids, gates, offs, sp[:R], pr[:R]
+
+
+def moe_grouped_mxfp4_gemm_combine(q, q_scale, act_fmt, T, topk, expert_offsets, sorted_pair, topk_ids, pair_row,
+                                   gates, w1, w1_scale, w2, w2_scale, out_dtype=torch.bfloat16, h=None,
+                                   h_scale=None, out=None):
     """Both expert FCs with FC2 fused into the gate-weighted combine (T <= 64).
     Returns (h, h_scale, out) with out [T][H]."""
     dev = _dev(q)
-    for t in (q_scale, expert_offsets, sorted_pair, gates, w1, w1_scale, w2, w2_scale):
+    for t in (q_scale, expert_offsets, sorted_pair, topk_ids, pair_row, gates, w1, w1_scale, w2, w2_scale):
         _dev(t)
     if w1.dim() != 3:
         raise RuntimeError("w1 must be [E][2I][H/2]")
@@ -333,6 +362,8 @@ def moe_grouped_mxfp4_gemm_combine(q, q_scale, act_fmt, T, topk, expert_offsets,
     _need(q_scale, "q_scale", torch.uint8, (T, H // 32))
     _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
     _need(sorted_pair, "sorted_pair", torch.int32, ((">=", R),))
+    _need(topk_ids, "topk_ids", torch.int32, (T, topk))
+    _need(pair_row, "pair_row", torch.int32, ((">=", R),))
     _need(gates, "gates", torch.float32, (T, topk))
     _need(w1, "w1", torch.uint8, (E, 2 * I, H // 2))
     _need(w1_scale, "w1_scale", torch.uint8, (E, 2 * I, H // 32))
@@ -350,8 +381,8 @@ def moe_grouped_mxfp4_gemm_combine(q, q_scale, act_fmt, T, topk, expert_offsets,
     _need(h_scale, "h_scale", torch.uint8, ((">=", R), I // 32))
     _need(out, "out", (torch.float32, torch.bfloat16), ((">=", T), H))
     _check(load().moe_grouped_mxfp4_gemm_combine(
-        _ptr(q), _ptr(q_scale), f, T, topk, H, I, E, _ptr(expert_offsets), _ptr(sorted_pair), _ptr(gates),
-        _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(h), _ptr(h_scale), _ptr(out),
+        _ptr(q), _ptr(q_scale), f, T, topk, H, I, E, _ptr(expert_offsets), _ptr(sorted_pair), _ptr(topk_ids),
+        _ptr(pair_row), _ptr(gates), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(h), _ptr(h_scale), _ptr(out),
         DTYPES[out.dtype], _stream(dev)), "moe_grouped_mxfp4_gemm_combine")
     return h[:R], h_scale[:R], out[:T]
 
@@ -359,13 +390,17 @@ def moe_grouped_mxfp4_gemm_combine(q, q_scale, act_fmt, T, topk, expert_offsets,
 def moe_layer(x, logits, w1, w1_scale, w2, w2_scale, topk, act_fmt="e4m3", y_dtype=torch.bfloat16,
               out_dtype=torch.bfloat16, fused=False):
     """The whole expert layer through the C-ABI calls (one stream, no host sync).
-    fused=True (T <= 64): FC2 and the combine in one kernel; y is not formed (None)."""
+    fused=True (T <= 64): quantisation and routing in one launch (E <= 256), FC2 and
+    the combine in one kernel; y is not formed (None)."""
     T = x.shape[0]
-    q, qs = mxfp4_quantize_act(x, act_fmt)
-    ids, gates, offs, sp, pr = moe_route_permute(logits, topk)
+    if fused and logits.shape[1] <= 256:
+        q, qs, ids, gates, offs, sp, pr = moe_quantize_route(x, logits, topk, act_fmt)
+    else:
+        q, qs = mxfp4_quantize_act(x, act_fmt)
+        ids, gates, offs, sp, pr = moe_route_permute(logits, topk)
     if fused:
-        h, hs, out = moe_grouped_mxfp4_gemm_combine(q, qs, act_fmt, T, topk, offs, sp, gates, w1, w1_scale, w2,
-                                                    w2_scale, out_dtype)
+        h, hs, out = moe_grouped_mxfp4_gemm_combine(q, qs, act_fmt, T, topk, offs, sp, ids, pr, gates, w1, w1_scale,
+                                                    w2, w2_scale, out_dtype)
         y = None
     else:
         h, hs, y = moe_grouped_mxfp4_gemm(q, qs, act_fmt, T, topk, offs, sp, w1, w1_scale, w2, w2_scale, y_dtype)

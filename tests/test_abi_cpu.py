@@ -134,16 +134,38 @@ def test_grouped_gemm_errors():
     assert call(T=0, q=None) == OK
 
 
+def test_quantize_route_errors():
+    lib = _lib()
+
+    def call(**kw):
+        a = dict(x=A, xd=1, lg=A, T=8, H=7168, E=256, k=6, fmt=0, q=A, qs=A, ids=A, g=A, off=A, sp=A, pr=A)
+        a.update(kw)
+        return lib.moe_quantize_route(a["x"], a["xd"], a["lg"], a["T"], a["H"], a["E"], a["k"], a["fmt"], a["q"],
+                                      a["qs"], a["ids"], a["g"], a["off"], a["sp"], a["pr"], None)
+
+    assert call(T=65) == UNSUPPORTED  # decode-sized batches only
+    assert call(E=257) == UNSUPPORTED
+    assert call(H=7168 + 16) == SHAPE
+    assert call(k=9) == SHAPE
+    assert call(k=7, E=6) == SHAPE
+    assert call(xd=3) == FORMAT
+    assert call(fmt=2) == FORMAT
+    assert call(lg=None) == NULL
+    assert call(off=None, T=0) == NULL  # the offsets are written even for no tokens
+    assert call(pr=U) == ALIGN
+    assert call(x=U) == ALIGN
+
+
 def test_fused_fc2_combine_errors():
     lib = _lib()
 
     def call(**kw):
-        a = dict(q=A, qs=A, fmt=1, T=8, k=6, H=7168, I=2048, E=256, off=A, sp=A, g=A, w1=A, s1=A, w2=A, s2=A,
-                 h=A, hs=A, out=A, od=1)
+        a = dict(q=A, qs=A, fmt=1, T=8, k=6, H=7168, I=2048, E=256, off=A, sp=A, ids=A, pr=A, g=A, w1=A, s1=A,
+                 w2=A, s2=A, h=A, hs=A, out=A, od=1)
         a.update(kw)
         return lib.moe_grouped_mxfp4_gemm_combine(
-            a["q"], a["qs"], a["fmt"], a["T"], a["k"], a["H"], a["I"], a["E"], a["off"], a["sp"], a["g"],
-            a["w1"], a["s1"], a["w2"], a["s2"], a["h"], a["hs"], a["out"], a["od"], None)
+            a["q"], a["qs"], a["fmt"], a["T"], a["k"], a["H"], a["I"], a["E"], a["off"], a["sp"], a["ids"],
+            a["pr"], a["g"], a["w1"], a["s1"], a["w2"], a["s2"], a["h"], a["hs"], a["out"], a["od"], None)
 
     assert call(T=65) == UNSUPPORTED  # decode-sized batches only
     assert call(H=7168 + 128) == SHAPE
@@ -155,6 +177,8 @@ def test_fused_fc2_combine_errors():
     assert call(E=4096) == UNSUPPORTED
     assert call(H=1 << 20, I=4096) == UNSUPPORTED  # one expert's w1 above 4 GiB
     assert call(g=None) == NULL
+    assert call(ids=None) == NULL
+    assert call(pr=U) == ALIGN
     assert call(out=None) == NULL
     assert call(g=U) == ALIGN
     assert call(out=U) == ALIGN

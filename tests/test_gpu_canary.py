@@ -106,7 +106,8 @@ def test_fused_fc2_combine_outputs_stay_inside_their_buffers(T, H, I, E, k, fmt,
     ops._check(lib.moe_route_permute(_p(logits), T, E, k, _p(b["ids"]), _p(b["gates"]), _p(b["offs"]), _p(b["sp"]),
                                      _p(b["pr"]), st), "route")
     ops._check(lib.moe_grouped_mxfp4_gemm_combine(
-        _p(b["q"]), _p(b["q_scale"]), f, T, k, H, I, E, _p(b["offs"]), _p(b["sp"]), _p(b["gates"]), _p(w1), _p(s1),
+        _p(b["q"]), _p(b["q_scale"]), f, T, k, H, I, E, _p(b["offs"]), _p(b["sp"]), _p(b["ids"]), _p(b["pr"]),
+        _p(b["gates"]), _p(w1), _p(s1),
         _p(w2), _p(s2), _p(b["h"]), _p(b["hs"]), _p(b["out"]), ops.DTYPES[out_dtype], st), "grouped+combine")
     torch.cuda.synchronize()
     for name, v in bufs.items():
