@@ -24,6 +24,7 @@ hardware counters into HBM bytes.
 
 import argparse
 import json
+import subprocess
 import os
 import sys
 import time
@@ -165,6 +166,58 @@ class Layer:
         ops._check(lib.moe_unpermute_combine(P(self.y), ops.DTYPES[self.y_dtype], P(self.gates), P(self.pr),
                                              self.T, self.k, c["H"], P(self.out), ops.MXF_BF16, st), "combine")
         if ev: ev[4].record()
+
+
+def kernel_times_us(step_fn, reps=3):
+    """Mean device time per step of each kernel, from torch's profiler (a separate,
+    untimed pass; {} if the profiler is unavailable)."""
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        step_fn(None)
+        torch.cuda.synchronize()
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for _ in range(reps):
+                step_fn(None)
+            torch.cuda.synchronize()
+        out = {}
+        for ev in prof.key_averages():
+            t = getattr(ev, "device_time_total", None)
+            if t is None:
+                t = getattr(ev, "cuda_time_total", 0.0)
+            if t and "mxf::" in ev.key:
+                out[ev.key] = out.get(ev.key, 0.0) + t / reps
+        return out
+    except Exception as ex:  # the report stays valid without it
+        log(f"[bench] kernel times unavailable: {ex}")
+        return {}
+
+
+def pick(times, *needles):
+    """Sum of the kernel times whose names contain every needle."""
+    v = sum(t for k, t in times.items() if all(n in k for n in needles))
+    return round(v, 2) if v else None
+
+
+def gpu_clocks():
+    """Current clocks as rocm-smi reports them (None if it cannot be run)."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        card = d[sorted(d)[0]]
+        return {k.strip(" :"): v for k, v in card.items() if "clk" in k.lower()}
+    except Exception:
+        return None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def ctypes_stream():
@@ -473,6 +526,21 @@ def main():
         })
         if ceil:
             result["frac_of_measured_ceiling"] = round(g_tflops / ceil["mfma_e2m1_random_TFLOPs"], 4)
+        # FC1 and FC2 apart (the grouped-GEMM call launches both): device times per step
+        # (the profiler's tracer lengthens these long kernels by 10-20 %, so its times give
+        # the split of the event-timed grouped-GEMM stage, not the times themselves)
+        kt = kernel_times_us(r["layer"].step)
+        fc1, fc2 = pick(kt, "<0,"), pick(kt, "<1,")
+        if fc1 and fc2:
+            fl1, fl2 = r["pairs"] * 58720256, r["pairs"] * 29360128
+            t1, t2 = g_ms * fc1 / (fc1 + fc2), g_ms * fc2 / (fc1 + fc2)
+            result["fc1_fc2"] = {"fc1_ms": round(t1, 4), "fc2_ms": round(t2, 4),
+                                 "fc1_TFLOPs": round(fl1 / t1 / 1e9, 1), "fc2_TFLOPs": round(fl2 / t2 / 1e9, 1),
+                                 "fc1_frac": round(fl1 / t1 / 1e9 / peak, 4), "fc2_frac": round(fl2 / t2 / 1e9 / peak, 4),
+                                 "profiler_us": {"fc1": fc1, "fc2": fc2},
+                                 "method": "grouped_gemm stage time split by the FC1 / FC2 kernel-time ratio "
+                                           "from torch.profiler (3 steps after the timed loops)"}
+        result["gpu_clocks_after_prefill"] = gpu_clocks()
         del r["layer"], r["sets"]
         torch.cuda.empty_cache()
     if args.only in (None, "decode"):
@@ -492,6 +560,11 @@ def main():
                             "bound": "hbm", "achieved": gbs(g_ms), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(gbs(g_ms) / PEAK_HBM_GBS, 4),
                             "traffic": measured_traffic(name + "_fused")}}
+        kt = kernel_times_us(r["layer"].step, reps=10)
+        dec["kernels_us"] = {"quantize_route": pick(kt, "quantize_route_kernel"),
+                             "fc1": pick(kt, "gemm_stream1_kernel", ", 0,"),
+                             "fc2_combine": pick(kt, "fc2_combine_kernel"),
+                             "source": "torch.profiler device times, 10 steps after the timed loops"}
         ug = u["stage_ms"]["grouped_gemm"]
         dec["unfused"] = {"ms_per_step": round(u["ms"], 4),
                           "stages_ms": {k: round(v, 4) for k, v in u["stage_ms"].items()},
@@ -543,6 +616,7 @@ def main():
     if not args.no_cpu and args.only in (None, "prefill"):
         log("[bench] timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline("moe_prefill_t16384_fp4")
+        result["cpu_baseline"]["cpu_model"] = cpu_model()
     print(json.dumps(result), flush=True)
 
 

@@ -203,17 +203,9 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
     if (nn == 0) return;
     const int m_unit = jb / nn;
     n_tile = n_lo + jb % nn;
-    if (kMode == kModeDense) {
-      row0 = (int64_t)m_unit * BM;
-      if (row0 >= a.M) return;
-      m = (int)(a.M - row0 < BM ? a.M - row0 : BM);
-    } else {
-      int loc;
-      find_unit<BM>(a.offsets, a.E, 0, m_unit, e, loc);
-      if (e < 0) return;
-      row0 = a.offsets[e] + (int64_t)loc * BM;
-      m = min(BM, a.offsets[e + 1] - (int)row0);
-    }
+    row0 = (int64_t)m_unit * BM;
+    if (row0 >= a.M) return;
+    m = (int)(a.M - row0 < BM ? a.M - row0 : BM);
   } else {
     int loc, n_grp;
     grouped_work_item<BM>(a.offsets, a.E, a.split, ntiles / ntg, x, jb, e, n_grp, loc);

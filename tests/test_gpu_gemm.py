@@ -68,3 +68,20 @@ def test_dense_is_deterministic():
     c1 = ops.mxfp4_gemm(a, w, s)
     c2 = ops.mxfp4_gemm(a, w, s)
     assert torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("M,K,fmt", [
+    (1, 512, "e4m3"), (16, 4096, "e2m1"), (64, 7168, "e4m3"),  # K slices summed in a second kernel
+    (100, 1024, "e2m1"), (130, 2048, "e4m3"),                   # M > 64: tiled kernels (N = K = 1024, 2048)
+])
+def test_dense_one_hot_weights_return_the_codes(M, K, fmt):
+    """Row n of W holds 1.0 at k = n (unit scales), so C[m, n] is the decoded activation
+    code a_hat[m, n] itself - one exact product, every other product zero: the codes
+    that reach the matrix instruction equal the oracle's, bit for bit, in every K slice."""
+    a = dg.activations(300 + M, M, K, outliers=True)
+    codes = np.zeros((K, K), np.uint8)
+    codes[np.arange(K), np.arange(K)] = 2  # E2M1 1.0
+    w, s = oracle.pack_e2m1(codes), np.full((K, K // 32), 127, np.uint8)
+    got = _run(a, w, s, fmt)
+    q, qs = oracle.moe.quantize_act(oracle.bf16_bits_to_f64(a), fmt)
+    assert np.array_equal(got, oracle.moe.decode_act(q, qs, fmt))
