@@ -15,8 +15,10 @@ against its roofline.
 The fp64 CPU oracle is timed on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--only prefill|decode|dense|skewed|variants|copy]
+                       [--only prefill|decode|dense|skewed|variants|copy|calib]
 
+--only calib runs the dense E2M1 GEMM 256 x 8192 x 7168 per step (no JSON line): an
+LDS-DMA kernel whose HBM reads are known, to check the FETCH_SIZE scale factor.
 --only copy runs a plain device-to-device copy of 1 GiB per step (no JSON line):
 the reference kernel of known byte count that scales the FETCH_SIZE / WRITE_SIZE
 hardware counters into HBM bytes.
@@ -44,12 +46,14 @@ PEAK_TFLOPS = {"e2m1": 10100.0, "e4m3": 5000.0}  # dense MXFP4 / MXFP8 (FP8 x FP
 FLOP_PER_PAIR = 2 * 7168 * 4096 + 2 * 2048 * 7168  # 88,080,384
 BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,352
 
-# HBM bytes per grouped-GEMM call (FC1 + FC2 launches) from rocprofv3 FETCH_SIZE / WRITE_SIZE
-# passes, scaled by a 1 GiB copy (2.0 x FETCH_SIZE + 1.0 x WRITE_SIZE; the passes and the
+# HBM bytes per grouped-GEMM call (its FC1 + FC2 launches; "_fused": FC1 + the fused FC2 and
+# combine) from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled by a 1 GiB copy (2.0 x
+# FETCH_SIZE + 1.0 x WRITE_SIZE, checked on an LDS-DMA GEMM of known bytes; the passes and the
 # calibration are in profiles/moe_layer_hbm_traffic.md). They hold only for the GEMM sources
 # they were measured on (sha-256 over GEMM_SOURCES): on any other source traffic = null.
-TRAFFIC_SRC_SHA256 = "d1136d728a94c1ff832ba1fb8b3ab2b52fd2df32fe3da2d2b0a0a81969af76db"
-TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8802236000, "moe_decode_t8": 1008487008}
+TRAFFIC_SRC_SHA256 = "6e6f4943713099b9358539f6d533f11e51a1a9998b242d912fda42e04f655238"
+TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8655855309, "moe_decode_t8_fused": 1022623436,
+                 "moe_decode_t8": 1008466226, "moe_prefill_t2048_zipf": 3333345894}
 
 
 GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "mx_codec.hpp",
@@ -168,9 +172,14 @@ class Layer:
         if ev: ev[4].record()
 
 
+KERNEL_TIMES = True  # set from --no-kernel-times
+
+
 def kernel_times_us(step_fn, reps=3):
     """Mean device time per step of each kernel, from torch's profiler (a separate,
-    untimed pass; {} if the profiler is unavailable)."""
+    untimed pass; {} if the profiler is unavailable or switched off)."""
+    if not KERNEL_TIMES:
+        return {}
     try:
         from torch.profiler import ProfilerActivity, profile
         step_fn(None)
@@ -478,8 +487,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
+    # no torch.profiler pass for the per-kernel split (for runs under an outside profiler)
+    ap.add_argument("--no-kernel-times", action="store_true")
     # one workload (or the copy reference kernel) instead of the default line
-    ap.add_argument("--only", choices=["prefill", "decode", "dense", "skewed", "variants", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "dense", "skewed", "variants", "copy", "calib"],
+                    default=None)
     # the achievable-rate probes run with the default line; with --only, on request
     ap.add_argument("--ceilings", action="store_true")
     args = ap.parse_args()
@@ -488,6 +500,8 @@ def main():
               "single-GPU kernel; no multi-GPU figure is measured.", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    global KERNEL_TIMES
+    KERNEL_TIMES = not args.no_kernel_times
     if args.only == "copy":
         n = 1 << 30
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -496,6 +510,23 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"[bench] copy: {args.warmup + args.steps} copies of {n} bytes")
+        return
+    if args.only == "calib":
+        # an LDS-DMA kernel whose HBM reads are known: the dense E2M1 GEMM with one 256-row
+        # unit (256 x 256 tiles, copies by buffer_load ... lds), where every weight tile is
+        # read by one workgroup and the activation codes are shared through L2
+        M, N, K = 256, 8192, 7168
+        a = bf16_dev(dg.activations(5, M, K))
+        w, s_ = (to_dev(t) for t in dg.dense_weights(5, N, K, 120, 128))
+        lib = ops.load()
+        ws = torch.empty(lib.mxfp4_gemm_workspace_bytes(M, N, K, ops.MXF_E2M1), dtype=torch.uint8, device="cuda")
+        c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        for i in range(args.warmup + args.steps):
+            ops.mxfp4_gemm(a, w, s_, "e2m1", out=c, workspace=ws)
+        torch.cuda.synchronize()
+        reads = N * K // 2 + N * K // 32 + M * K // 2 + M * K // 32
+        log(f"[bench] calib: {args.warmup + args.steps} dense E2M1 GEMMs {M}x{N}x{K}; the GEMM kernel reads "
+            f"{reads} bytes (weights, their scales, activation codes and scales, each once) and writes {M * N * 4}")
         return
     ops.load()
     torch.cuda.synchronize()
@@ -593,6 +624,7 @@ def main():
                             "touched_weight_GBps_grouped": round(r["wbytes"] / (g_ms * 1e-3) / 1e9, 1)}
         sk = result["skewed"]
         sk["frac_fp8_peak"] = round(sk["grouped_TFLOPs"] / PEAK_TFLOPS["e4m3"], 4)
+        sk["traffic_grouped_gemm"] = measured_traffic(name)
         sk["frac_hbm_peak"] = round(sk["touched_weight_GBps_grouped"] / PEAK_HBM_GBS, 4)
         if ceil:
             sk["frac_of_measured_ceilings"] = {
