@@ -194,6 +194,15 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 #endif
 }
 
+// two fp32 values as packed bf16 bits (x in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t bf16x2_bits(float x, float y) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 r = __builtin_convertvector((f2){x, y}, b2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 template <bool kYBF16>
 __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
   if (kYBF16)
