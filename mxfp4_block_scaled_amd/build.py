@@ -31,7 +31,7 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-function",
 ]
-SOURCES = ["quantize.hip", "route.hip", "gemm.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "gemm_w4a16.hip", "gemm_q8.hip", "fc2_combine.hip", "combine.hip", "ceilings.hip", "abi.cpp", "noalloc.hip"]
+SOURCES = ["quantize.hip", "route.hip", "gemm.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "gemm_f8ring.hip", "gemm_w4a16.hip", "gemm_q8.hip", "fc2_combine.hip", "combine.hip", "ceilings.hip", "abi.cpp", "noalloc.hip"]
 
 
 def _compile(src, verbose):

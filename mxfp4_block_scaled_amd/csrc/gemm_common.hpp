@@ -326,9 +326,9 @@ __device__ __forceinline__ int buf_load4(buf_rsrc r, uint32_t voff, uint32_t sof
 #endif
 }
 
-// tile geometry of the LDS-ring kernels: 128 activation rows x 256 weight rows
+// tile geometry of the LDS-ring kernels: 256 activation rows x 256 weight rows
 namespace tile {
-constexpr int BM = 128, BN = 256;
+constexpr int BM = 256, BN = 256;
 }  // namespace tile
 
 // c[i] = sum over s < S of part[s * n + i], in the order s = 0 .. S-1 (n % 4 == 0)
@@ -342,5 +342,6 @@ void launch_stream_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, 
 int launch_tile_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int64_t rows, int64_t groups,
                      hipStream_t stream);
 void launch_wide_gemm(int mode, bool y_bf16, const GemmArgs& a, int64_t m_units, hipStream_t stream);
+void launch_f8ring_gemm(int mode, bool y_bf16, const GemmArgs& a, int64_t m_units, hipStream_t stream);
 
 }  // namespace mxf
