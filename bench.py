@@ -51,13 +51,13 @@ BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,
 # FETCH_SIZE + 1.0 x WRITE_SIZE, checked on an LDS-DMA GEMM of known bytes; the passes and the
 # calibration are in profiles/moe_layer_hbm_traffic.md). They hold only for the GEMM sources
 # they were measured on (sha-256 over GEMM_SOURCES): on any other source traffic = null.
-TRAFFIC_SRC_SHA256 = "6e6f4943713099b9358539f6d533f11e51a1a9998b242d912fda42e04f655238"
-TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8655855309, "moe_decode_t8_fused": 1022623436,
-                 "moe_decode_t8": 1008466226, "moe_prefill_t2048_zipf": 3333345894}
+TRAFFIC_SRC_SHA256 = "7317a2eb77c562291a5584026d4cbfe8fa1e47d44c8f618e79d4b493ba9b61f3"
+TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 9561447936, "moe_decode_t8_fused": 1022630810,
+                 "moe_decode_t8": 1008466842, "moe_prefill_t2048_zipf": 3167252787}
 
 
-GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "mx_codec.hpp",
-                "fc2_combine.hip")
+GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "gemm_f8ring.hip",
+                "tile256.hpp", "mx_codec.hpp", "fc2_combine.hip")
 
 
 def gemm_sources_sha256():
@@ -208,7 +208,10 @@ def pick(times, *needles):
 
 
 def gpu_clocks():
-    """Current clocks as rocm-smi reports them (None if it cannot be run)."""
+    """Current clocks as rocm-smi reports them (None if it cannot be run, and not
+    asked for in runs under an outside profiler: --no-kernel-times)."""
+    if not KERNEL_TIMES:
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
         d = json.loads(r.stdout)
