@@ -42,7 +42,7 @@ def _p(t):
 @pytest.mark.parametrize("T,H,I,E,k,fmt,routing,y_dtype", [
     (8, 1024, 512, 16, 6, "e4m3", "normal", torch.bfloat16),    # decode: streaming kernels
     (13, 1024, 2048, 16, 6, "e2m1", "normal", torch.float32),   # decode FP4, fp32 y, FC2 two row blocks
-    (301, 1024, 512, 8, 6, "e4m3", "normal", torch.bfloat16),   # FP8 128-row tiles, ragged
+    (301, 1024, 512, 8, 6, "e4m3", "normal", torch.bfloat16),   # FP8 256-row ring tiles, ragged
     (333, 1024, 1024, 32, 4, "e2m1", "normal", torch.float32),  # FP4 256-row tiles, fp32 y
     (700, 2048, 2048, 4, 2, "e2m1", "normal", torch.bfloat16),  # FP4, K = 2048 chained n-tiles
     (241, 1024, 1024, 64, 2, "e4m3", "zipf", torch.bfloat16),   # split: streamed small experts + tiles
@@ -118,7 +118,7 @@ def test_fused_fc2_combine_outputs_stay_inside_their_buffers(T, H, I, E, k, fmt,
 @pytest.mark.parametrize("M,N,K,fmt", [
     (37, 48, 5120, "e2m1"),   # M <= 64: K slices summed through the workspace
     (64, 4096, 7168, "e4m3"),  # the dense 64 x 4096 x 7168 shape
-    (70, 256, 1536, "e4m3"),   # FP8 128-row tiles, ragged
+    (70, 256, 1536, "e4m3"),   # FP8 256-row ring tiles, ragged
     (300, 512, 1536, "e2m1"),  # FP4 256-row tiles, ragged
     (129, 96, 512, "e4m3"),    # N % 256 != 0: streamed in 64-row chunks
 ])

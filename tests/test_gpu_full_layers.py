@@ -5,7 +5,7 @@ V4】Triton FP4 优化实战", "为什么中文对、英文错？" and the lesso
 kernel can be wrong for some experts and look right for the prompts that avoid
 them). So at the 16384-token FP4 layer (uniform routing: all 256 experts, one or
 two 256-row units each) and the 2048-token Zipf-routed FP8 layer (experts of
-1..16 rows streamed, larger ones in 128-row tiles), the oracle computes the first
+1..16 rows streamed, larger ones in 256-row ring tiles), the oracle computes the first
 and the last row of every row unit of every touched expert (every row of a
 streamed expert), and every row of the tokens that own them:
 
@@ -111,5 +111,5 @@ def test_fp4_prefill_16384_tokens_every_expert():
 
 
 def test_zipf_prefill_2048_tokens_every_touched_expert():
-    # E4M3 activations: experts of <= 16 rows streamed, the others in 128-row tiles
+    # E4M3 activations: experts of <= 16 rows streamed, the others in 256-row ring tiles
     _run_and_check("moe_prefill_t2048_zipf", unit=128, stream_max=16)

@@ -64,7 +64,7 @@ def _compare(g, ref, x, logits, w1, s1, w2, s2, k, fmt, rows=None, tokens=None):
 @pytest.mark.parametrize("T,H,I,E,k,fmt,seed", [
     (8, 1024, 512, 16, 6, "e4m3", 0),      # decode-shaped: weight-streaming kernel
     (40, 1536, 1024, 8, 3, "e2m1", 1),     # 40 tokens: streaming kernel, several rows per expert
-    (300, 1024, 512, 8, 6, "e4m3", 2),     # LDS-tiled kernel, several 128-row tiles, ragged tails
+    (300, 1024, 512, 8, 6, "e4m3", 2),     # LDS-ring kernels, several 256-row units, ragged tails
     (333, 1024, 1024, 32, 4, "e2m1", 3),   # FP4 x FP4 tiles, some experts empty
     (65, 512, 512, 4, 2, "e4m3", 4),       # just past the streaming threshold
     (700, 2048, 512, 4, 2, "e2m1", 5),     # FP4 x FP4, ~350 rows per expert: full and partial 256-row units
