@@ -137,7 +137,7 @@ def test_layer_fp32_y(T):
 
 
 def test_layer_fp32_y_fp8_tiles():
-    # FP8 activations past 64 tokens: register-streamed tiles, FC2 with fp32 y and K = I = 2048
+    # FP8 activations past 64 tokens: the 256 x 256 FP8 ring, FC2 with fp32 y and K = I = 2048
     T, H, I, E, k = 200, 1024, 2048, 8, 3
     x = dg.activations(14, T, H)
     logits = dg.logits(14, T, E, "normal")
