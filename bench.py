@@ -51,9 +51,9 @@ BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,
 # FETCH_SIZE + 1.0 x WRITE_SIZE, checked on an LDS-DMA GEMM of known bytes; the passes and the
 # calibration are in profiles/moe_layer_hbm_traffic.md). They hold only for the GEMM sources
 # they were measured on (sha-256 over GEMM_SOURCES): on any other source traffic = null.
-TRAFFIC_SRC_SHA256 = "7317a2eb77c562291a5584026d4cbfe8fa1e47d44c8f618e79d4b493ba9b61f3"
-TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 9561447936, "moe_decode_t8_fused": 1022630810,
-                 "moe_decode_t8": 1008466842, "moe_prefill_t2048_zipf": 3167252787}
+TRAFFIC_SRC_SHA256 = "dbf2a3b56ae687ebf1c641ecad15ca54783668ba19cfbcac7909246905b54b5a"
+TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8843126000, "moe_decode_t8_fused": 1022605763,
+                 "moe_decode_t8": 1008465412, "moe_prefill_t2048_zipf": 3165153536}
 
 
 GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "gemm_f8ring.hip",
