@@ -40,6 +40,10 @@ def test_dense_workloads(name):
     # E4M3 activations, M > 64, N % 256 == 0 at the layer's K values (fp32 C: the loop instance)
     (130, 256, 7168, "e4m3"), (100, 512, 2048, "e4m3"),
     (260, 256, 7168, "e2m1"),  # E2M1, 256 x 256 tiles, K = 7168 (fully unrolled stages), 4-row tail unit
+    # E4M3 on the 256 x 256 ring of 128-k stages: one full unit with K = 512 (four stages:
+    # a three-slot turn and one more), 65 rows (the second row group holds a single row),
+    # and 513 rows at K = 2048 (the unrolled 16-stage instance, a 1-row third unit)
+    (256, 256, 512, "e4m3"), (65, 512, 1024, "e4m3"), (513, 256, 2048, "e4m3"),
 ])
 def test_dense_ragged_shapes(M, N, K, fmt):
     a = dg.activations(M * 7 + N, M, K, outliers=True)
@@ -73,6 +77,7 @@ def test_dense_is_deterministic():
 @pytest.mark.parametrize("M,K,fmt", [
     (1, 512, "e4m3"), (16, 4096, "e2m1"), (64, 7168, "e4m3"),  # K slices summed in a second kernel
     (100, 1024, "e2m1"), (130, 2048, "e4m3"),                   # M > 64: tiled kernels (N = K = 1024, 2048)
+    (70, 7168, "e4m3"),                                          # the FP8 ring's unrolled 56-stage instance
 ])
 def test_dense_one_hot_weights_return_the_codes(M, K, fmt):
     """Row n of W holds 1.0 at k = n (unit scales), so C[m, n] is the decoded activation
