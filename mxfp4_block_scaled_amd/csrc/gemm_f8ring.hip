@@ -254,7 +254,7 @@ __global__ void __launch_bounds__(512) gemm_f8ring_kernel(GemmArgs a) {
 
 template <int kMode, bool kYBF16>
 static void launch_f8ring_t(const GemmArgs& a, int64_t m_units, hipStream_t stream) {
-  const dim3 grid((unsigned)(8 * cdiv(a.ntiles, 8) * m_units));
+  const dim3 grid = tile256_grid(kMode, a, m_units, 1);
   // fully unrolled instances for K = 7168 and K = 2048 (the layer's H and I)
   const int64_t nst = a.K / f8r::KS;
   if (nst == 56) gemm_f8ring_kernel<kMode, kYBF16, 56><<<grid, 512, 0, stream>>>(a);

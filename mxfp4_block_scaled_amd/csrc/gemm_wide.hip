@@ -314,20 +314,22 @@ __global__ void __launch_bounds__(512) gemm_wide_kernel(GemmArgs a) {
 }
 
 template <int kMode, bool kYBF16>
-static void launch_wide_t(const GemmArgs& a, int64_t m_units, hipStream_t stream) {
-  const dim3 grid((unsigned)(8 * cdiv(a.ntiles, 8) * m_units));
+static void launch_wide_t(const GemmArgs& a_in, int64_t m_units, hipStream_t stream) {
   // fully unrolled instances for K = 7168 and K = 2048 (the layer's H and I)
+  GemmArgs a = a_in;
   const int64_t nst = a.K / wide::KS;
   if constexpr (kMode != kModeDense) {
     if (nst == 8 && a.ngroup == 4) {
-      gemm_wide_kernel<kMode, kYBF16, 8, 4><<<grid, 512, 0, stream>>>(a);
+      gemm_wide_kernel<kMode, kYBF16, 8, 4><<<tile256_grid(kMode, a, m_units, 4), 512, 0, stream>>>(a);
       return;
     }
     if (nst == 8 && a.ngroup == 2) {
-      gemm_wide_kernel<kMode, kYBF16, 8, 2><<<grid, 512, 0, stream>>>(a);
+      gemm_wide_kernel<kMode, kYBF16, 8, 2><<<tile256_grid(kMode, a, m_units, 2), 512, 0, stream>>>(a);
       return;
     }
   }
+  a.ngroup = 1;
+  const dim3 grid = tile256_grid(kMode, a, m_units, 1);
   if (nst == 28) gemm_wide_kernel<kMode, kYBF16, 28, 1><<<grid, 512, 0, stream>>>(a);
   else if (nst == 8) gemm_wide_kernel<kMode, kYBF16, 8, 1><<<grid, 512, 0, stream>>>(a);
   else gemm_wide_kernel<kMode, kYBF16, 0, 1><<<grid, 512, 0, stream>>>(a);

@@ -12,6 +12,17 @@ namespace mxf {
 // 8 x 4352 B (fp32)
 constexpr int kTile256Staging = 8 * 8192;
 
+// Blocks of the launch: dense, XCD x walks nn <= ceil(ntiles / 8) n-tiles for each of
+// the m_units row units; grouped, XCD x runs items [x T / 8, (x + 1) T / 8) of the
+// T = units x ntiles / ntg items (units <= m_units), so ceil(m_units ntiles / ntg / 8)
+// blocks per XCD cover them. Blocks past their XCD's range exit at once, but each
+// still waits for a whole compute unit (the ring takes all of its LDS), so the grid
+// follows the n-tiles per workgroup.
+inline dim3 tile256_grid(int mode, const GemmArgs& a, int64_t m_units, int ntg) {
+  const int64_t per_xcd = mode == kModeDense ? cdiv(a.ntiles, 8) * m_units : cdiv(m_units * (a.ntiles / ntg), 8);
+  return dim3((unsigned)(8 * per_xcd));
+}
+
 // Epilogue of one 256 x 256 tile, straight from the accumulators (FC1 without LDS). The
 // MFMAs take the weight fragment as their first operand, so acc[fm][fn][v] of
 // lane l is token row 64 wm + 32 fm + l % 32 and output column c(fn) + 8 (v / 4)
