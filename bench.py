@@ -51,9 +51,9 @@ BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,
 # FETCH_SIZE + 1.0 x WRITE_SIZE, checked on an LDS-DMA GEMM of known bytes; the passes and the
 # calibration are in profiles/moe_layer_hbm_traffic.md). They hold only for the GEMM sources
 # they were measured on (sha-256 over GEMM_SOURCES): on any other source traffic = null.
-TRAFFIC_SRC_SHA256 = "dbf2a3b56ae687ebf1c641ecad15ca54783668ba19cfbcac7909246905b54b5a"
-TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8843126000, "moe_decode_t8_fused": 1022605763,
-                 "moe_decode_t8": 1008465412, "moe_prefill_t2048_zipf": 3165153536}
+TRAFFIC_SRC_SHA256 = "b6b6a097a31c415146c1cd207265ea6ca9c1fd4df813573b734973b1da8a4a17"
+TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8844413760, "moe_decode_t8_fused": 1022553481,
+                 "moe_decode_t8": 1008462349, "moe_prefill_t2048_zipf": 3168333104}
 
 
 GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "gemm_f8ring.hip",
