@@ -42,6 +42,10 @@ from mxfp4_block_scaled_amd import ops  # noqa: E402
 
 METRIC = "MoE MXFP4 grouped-GEMM TFLOP/s (prefill) & weight GB/s (decode) vs roofline"
 PEAK_HBM_GBS = 8000.0
+# bytes the probe's stage moves into LDS; the 256 x 256 FP4 ring kernel's stage moves 64 KB
+# of codes plus 4 KB of scales (a 16 KB scale group every 4 stages)
+LDS_FILL_STAGE_BYTES = 65536
+RING_STAGE_BYTES = 65536 + 4096
 PEAK_TFLOPS = {"e2m1": 10100.0, "e4m3": 5000.0}  # dense MXFP4 / MXFP8 (FP8 x FP4 runs at the FP8 rate)
 FLOP_PER_PAIR = 2 * 7168 * 4096 + 2 * 2048 * 7168  # 88,080,384
 BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,352
@@ -304,7 +308,8 @@ def bench_moe(name, steps, warmup, rotate, fused=False, sets=None):
     flops = pairs * FLOP_PER_PAIR
     wbytes = touched * BYTES_PER_EXPERT
     return dict(cfg=cfg, ms=wall * 1e3, stage_ms=stage_ms, touched=touched, pairs=pairs, flops=flops,
-                wbytes=wbytes, max_rows=int(counts.max()), layer=layer, sets=sets)
+                wbytes=wbytes, max_rows=int(counts.max()), units256=int(((counts + 255) // 256).sum()),
+                layer=layer, sets=sets)
 
 
 def bench_dense(steps, warmup, rotate=48, name="dense_m64_n4096_k7168"):
@@ -409,9 +414,10 @@ def bench_fp4_variants(steps, warmup, rotate=48):
 
 
 def measure_ceilings(reps=3):
-    """What this GPU sustains for the two bounds (include/mxf_ceilings.h), best of
-    `reps`: a non-temporal streaming read of 2 GiB, and register-only loops of
-    32x32x64 scaled MFMAs on random operand bits (E2M1 x E2M1, E4M3 x E2M1)."""
+    """What this GPU sustains for the bounds (include/mxf_ceilings.h), best of `reps`:
+    a non-temporal streaming read of 2 GiB, register-only loops of 32x32x64 scaled
+    MFMAs on random operand bits (E2M1 x E2M1, E4M3 x E2M1), and the HBM -> LDS copy
+    path alone (own bytes / the FC1 launch's sharing)."""
     lib = ops.load()
     st = ctypes_stream()
     buf = torch.ones(1 << 29, dtype=torch.int32, device="cuda")  # 2 GiB
@@ -442,6 +448,15 @@ def measure_ceilings(reps=3):
         ms = best(lambda: ops._check(lib.mxf_ceiling_mfma(f, ops._ptr(words), words.numel(), 124, iters,
                                                           ops._ptr(sink), st), "mfma"))
         out[key] = round(flops / (ms * 1e-3) / 1e12, 1)
+    # the prefill GEMMs' operand copies on their own: 28 stages of 64 KB into LDS per
+    # workgroup, each workgroup reading its own bytes (HBM streaming) or sharing them as
+    # the grouped FC1 launch does (16 workgroups per activation unit, 2 per weight tile)
+    sm = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for key, pattern, groups in (("lds_fill_own_GBps", 0, 1024), ("lds_fill_fc1_sharing_GBps", 1, 2048)):
+        assert lib.mxf_ceiling_lds_copy_bytes(pattern, groups) <= nbytes
+        ms = best(lambda: ops._check(lib.mxf_ceiling_lds_copy(ops._ptr(buf), nbytes, pattern, groups, ops._ptr(sm),
+                                                              st), "lds_copy"))
+        out[key] = round(groups * LDS_FILL_STAGE_BYTES * ops.CEILING_COPY_STAGES / (ms * 1e-3) / 1e9, 1)
     del buf
     torch.cuda.empty_cache()
     return out
@@ -574,6 +589,16 @@ def main():
                                  "profiler_us": {"fc1": fc1, "fc2": fc2},
                                  "method": "grouped_gemm stage time split by the FC1 / FC2 kernel-time ratio "
                                            "from torch.profiler (3 steps after the timed loops)"}
+            # the copy path: bytes the ring kernels move into LDS per call (units x n-tiles x
+            # stages x 68 KB) over each kernel's time, against the copy probe's rate
+            u = r["units256"]
+            b1 = u * (2 * cfg["I"] // 256) * (cfg["H"] // 256) * RING_STAGE_BYTES
+            b2 = u * (cfg["H"] // 256) * (cfg["I"] // 256) * RING_STAGE_BYTES
+            lf = {"units": u, "fc1_bytes": b1, "fc2_bytes": b2,
+                  "fc1_GBps": round(b1 / t1 / 1e6, 1), "fc2_GBps": round(b2 / t2 / 1e6, 1)}
+            if ceil:
+                lf["fc1_frac_of_sharing_ceiling"] = round(b1 / t1 / 1e6 / ceil["lds_fill_fc1_sharing_GBps"], 4)
+            result["lds_fill"] = lf
         result["gpu_clocks_after_prefill"] = gpu_clocks()
         del r["layer"], r["sets"]
         torch.cuda.empty_cache()

@@ -47,6 +47,8 @@ SIGNATURES = {
     "mxf_ceiling_mfma_flops": (_c_i64, [_c_int]),
     "mxf_ceiling_mfma": (_c_int, [_c_int, _p, _c_i64, _c_int, _c_int, _p, _p]),
     "mxf_ceiling_read": (_c_int, [_p, _c_i64, _p, _p]),
+    "mxf_ceiling_lds_copy_bytes": (_c_i64, [_c_int, _c_int]),
+    "mxf_ceiling_lds_copy": (_c_int, [_p, _c_i64, _c_int, _c_int, _p, _p]),
 }
 
 CEILING_MFMA_GROUPS = 512
@@ -432,3 +434,21 @@ def ceiling_read(buf, xor_out=None):
     nbytes = buf.numel() * buf.element_size()
     _check(load().mxf_ceiling_read(_ptr(buf), nbytes, _ptr(xor_out), _stream(dev)), "mxf_ceiling_read")
     return xor_out
+
+
+CEILING_COPY_STAGES = 28
+CEILING_COPY_REGION = CEILING_COPY_STAGES * 32768
+
+
+def ceiling_lds_copy(buf, pattern, groups, sum_out=None):
+    """HBM -> LDS copy-path probe (include/mxf_ceilings.h): `groups` workgroups each fill
+    28 stages of 64 KB from their two regions of buf (pattern 0: their own; pattern 1:
+    shared as in the grouped FC1 launch). Returns the int32 tensor holding the sum, mod
+    2^32, of every 32-bit word read (accumulated into sum_out when given)."""
+    dev = _dev(buf)
+    if sum_out is None:
+        sum_out = torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = buf.numel() * buf.element_size()
+    _check(load().mxf_ceiling_lds_copy(_ptr(buf), nbytes, pattern, groups, _ptr(sum_out), _stream(dev)),
+           "mxf_ceiling_lds_copy")
+    return sum_out

@@ -209,6 +209,18 @@ def test_ceiling_probe_errors():
     assert lib.mxf_ceiling_read(None, 64, A, None) == NULL
     assert lib.mxf_ceiling_read(U, 64, A, None) == ALIGN
     assert lib.mxf_ceiling_read(None, 0, None, None) == OK
+    R = ops.CEILING_COPY_REGION
+    assert R == 28 * 32768
+    assert lib.mxf_ceiling_lds_copy_bytes(0, 1024) == 2 * 1024 * R
+    assert lib.mxf_ceiling_lds_copy_bytes(1, 2048) == (128 + 1024) * R
+    assert lib.mxf_ceiling_lds_copy_bytes(1, 100) == 0 and lib.mxf_ceiling_lds_copy_bytes(2, 256) == 0
+    assert lib.mxf_ceiling_lds_copy_bytes(0, 65536 + 256) == 0
+    assert lib.mxf_ceiling_lds_copy(A, 2 * 256 * R - 16, 0, 256, A, None) == SHAPE
+    assert lib.mxf_ceiling_lds_copy(A, 1 << 40, 1, 255, A, None) == SHAPE
+    assert lib.mxf_ceiling_lds_copy(A, 1 << 40, 3, 256, A, None) == SHAPE
+    assert lib.mxf_ceiling_lds_copy(None, 1 << 40, 0, 256, A, None) == NULL
+    assert lib.mxf_ceiling_lds_copy(A, 1 << 40, 0, 256, None, None) == NULL
+    assert lib.mxf_ceiling_lds_copy(U, 1 << 40, 0, 256, A, None) == ALIGN
 
 
 def test_noalloc_gemm_rejects_before_touching_the_device():

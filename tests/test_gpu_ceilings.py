@@ -1,7 +1,9 @@
 """The achievable-rate probes (include/mxf_ceilings.h) compute what they claim:
 the streaming read visits every byte (its XOR of all 32-bit words equals the
-host's), and the MFMA loop with all operands 1.0 and scale 2^0 accumulates
-64 per element per instruction exactly."""
+host's), the MFMA loop with all operands 1.0 and scale 2^0 accumulates 64 per
+element per instruction exactly, and the LDS-fill probe lands every byte of every
+region it copies, as often as its sharing pattern says (its wrapping sum of the
+words it read equals the one torch computes from the regions)."""
 
 import numpy as np
 import pytest
@@ -45,3 +47,22 @@ def test_mfma_probe_random_operands_run(fmt):
     sink, _ = ops.ceiling_mfma(words, fmt, 124, 100)
     torch.cuda.synchronize()
     assert sink.shape == (512,)
+
+
+@pytest.mark.parametrize("pattern,groups", [(0, 256), (1, 256), (1, 512)])
+def test_lds_copy_probe_lands_every_region(pattern, groups):
+    lib = ops.load()
+    nbytes = lib.mxf_ceiling_lds_copy_bytes(pattern, groups)
+    R = ops.CEILING_COPY_REGION
+    g = torch.Generator(device="cuda").manual_seed(groups + pattern)
+    words = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda", generator=g)
+    got = ops.ceiling_lds_copy(words, pattern, groups)
+    torch.cuda.synchronize()
+    region_sums = words.view(-1, R // 4).to(torch.int64).sum(dim=1)   # one per region
+    if pattern == 0:
+        want = int(region_sums.sum().item())
+    else:
+        na = groups // 16
+        want = 16 * int(region_sums[:na].sum().item()) + 2 * int(region_sums[na:].sum().item())
+    assert (int(got.item()) & 0xFFFFFFFF) == (want & 0xFFFFFFFF)
+
