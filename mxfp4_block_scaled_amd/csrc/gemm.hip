@@ -17,6 +17,40 @@ int dense_ksplit(int64_t M, int64_t N, int64_t K) {
   return (int)(nss > 4 ? cdiv(nss, 4) : 1);
 }
 
+int dense_q_ksplit(int64_t M, int64_t N, int64_t K) {
+  // a weight matrix of at most 1 MiB of codes is streamed by few workgroups over the
+  // whole K in one launch (the slices' second launch would cost more than it saves)
+  if (N * (K / 2) <= ((int64_t)1 << 20)) return 1;
+  return dense_ksplit(M, N, K);
+}
+
+int launch_dense_q_gemm(const uint16_t* a16, bool act_fp4, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+                        const uint8_t* w_scale, float* c, float* partials, hipStream_t stream) {
+  if (M == 0) return 0;
+  if (M > kDenseQRows) return -1;
+  GemmArgs a{};
+  a.act = reinterpret_cast<const uint8_t*>(a16);
+  a.act_rows = M;
+  a.M = M;
+  a.w = w;
+  a.w_scale = w_scale;
+  a.K = K;
+  a.N = N;
+  a.E = 1;
+  a.topk = 1;
+  const int S = dense_q_ksplit(M, N, K);
+  if (S > 1) {
+    a.out = partials;
+    a.kchunk = 4;
+    launch_stream_q_gemm(act_fp4, a, dim3((unsigned)cdiv(N, 64), (unsigned)S), stream);
+    launch_reduce_partials(partials, S, M * N, c, stream);
+  } else {
+    a.out = c;
+    launch_stream_q_gemm(act_fp4, a, dim3((unsigned)cdiv(N, 64), 1), stream);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_dense_gemm(const uint8_t* qa, const uint8_t* qa_scale, bool act_fp4, int64_t M, int64_t N, int64_t K,
                       const uint8_t* w, const uint8_t* w_scale, float* c, float* partials, hipStream_t stream) {
   if (M == 0) return 0;

@@ -337,6 +337,8 @@ void launch_reduce_partials(const float* part, int S, int64_t n, float* c, hipSt
 // kernel launchers (gemm_stream.hip, gemm_tile.hip); mode is kModeFC1 / kModeFC2 / kModeDense
 void launch_stream_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int mt, dim3 grid,
                         hipStream_t stream);
+// dense GEMM with M <= 16 whose a.act holds the bf16 activations [M][K] (quantised in registers)
+void launch_stream_q_gemm(bool act_fp4, const GemmArgs& a, dim3 grid, hipStream_t stream);
 // rows: activation rows in all; groups: experts that may hold a partial unit (0 for dense)
 // returns -1 (nothing launched) when an operand exceeds the tiled kernels' 32-bit offsets
 int launch_tile_gemm(int mode, bool y_bf16, bool act_fp4, const GemmArgs& a, int64_t rows, int64_t groups,

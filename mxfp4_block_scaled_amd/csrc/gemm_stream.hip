@@ -51,6 +51,117 @@ __device__ __forceinline__ void epilogue_fc1(const float (&tot)[4][4], int local
 }
 
 // ---------------------------------------------------------------------------------
+// Activation quantisation inside the dense GEMM (M <= 16): a lane loads the bf16
+// values its MFMA operand holds and encodes them in registers, so the codes never
+// leave the compute unit.
+
+// largest bf16 magnitude (as bits) among the 8 bf16 values of x
+__device__ __forceinline__ uint32_t bf16_absmax8(v4i x) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t u = (uint32_t)x[i] & 0x7FFF7FFFu;
+    m = max(m, max(u & 0xFFFFu, u >> 16));
+  }
+  return m;
+}
+
+// 16 bf16 values (k order, x0 then x1) -> 16 E4M3 codes (4 words, little-endian k
+// order) at scale byte `byte`, by gfx950's scaled FP8 conversion (value / scale, round
+// to nearest even on the E4M3 grid, subnormals included). That conversion does not
+// saturate, so every value is first clamped to +-448 x scale: with it the codes are
+// the saturating ones of the block rule. Blocks with a scale byte below 64 are lifted
+// by 2^64 (values and scale alike, exact) so that the scale and the values stay
+// normal fp32 numbers.
+__device__ __forceinline__ void e4m3_encode16(v4i x0, v4i x1, uint32_t byte, uint32_t (&out)[4]) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const bool lift = byte < 64u;
+  const float sc = __uint_as_float((byte + (lift ? 64u : 0u)) << 23);
+  const float lim = 448.0f * sc;
+  const bool any_lift = __builtin_amdgcn_ballot_w64(lift) != 0;
+  const float mul = lift ? 18446744073709551616.0f : 1.0f;
+  const uint32_t w[8] = {(uint32_t)x0[0], (uint32_t)x0[1], (uint32_t)x0[2], (uint32_t)x0[3],
+                         (uint32_t)x1[0], (uint32_t)x1[1], (uint32_t)x1[2], (uint32_t)x1[3]};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float v[4] = {__uint_as_float(w[2 * j] << 16), __uint_as_float(w[2 * j] & 0xFFFF0000u),
+                  __uint_as_float(w[2 * j + 1] << 16), __uint_as_float(w[2 * j + 1] & 0xFFFF0000u)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (any_lift) v[i] *= mul;
+      v[i] = __builtin_amdgcn_fmed3f(v[i], -lim, lim);
+    }
+    v2s o = {0, 0};
+#if defined(__HIP_DEVICE_COMPILE__)
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, v[0], v[1], sc, false);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, v[2], v[3], sc, true);
+#endif
+    out[j] = __builtin_bit_cast(uint32_t, o);
+  }
+}
+
+// One 16-row fragment of a 512-k super-step from bf16 (raw: the 16 16-byte loads of
+// the lane, 4 per MFMA step s) to the MFMA operands: aq[s] codes, as the 4 scale bytes
+// (byte s = block 4 s + g of the super-step, the lane's own block index). Lane (g, r16):
+//   E2M1: raw[4 s .. 4 s + 3] are k 128 s + 32 g + [0, 32): one whole block;
+//   E4M3: raw[4 s], raw[4 s + 1] are k 128 s + 16 g + [0, 16) (block 4 s + g / 2) and
+//         raw[4 s + 2], raw[4 s + 3] are k 128 s + 64 + 16 g + [0, 16) (block
+//         4 s + 2 + g / 2): each block is split between lanes g and g ^ 1 (lane ^ 16),
+//         which exchange their half-block amax; the scale byte of block 4 s + g then
+//         sits with lane g itself (g = 0: low half, g = 3: high half) or with the
+//         partner lane ^ 48 (g = 1 takes g = 2's low-half byte, g = 2 takes g = 1's
+//         high-half byte).
+// Rows past the GEMM's M (valid false) give zero codes and scales.
+template <bool kActFP4>
+__device__ __forceinline__ void quantize_fragment(const v4i (&raw)[16], bool valid, v8i (&aq)[4], int& as) {
+  const int g = (threadIdx.x & 63) >> 4;
+  uint32_t lo_b = 0, hi_b = 0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if constexpr (kActFP4) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t u = (uint32_t)raw[4 * s + i][j];
+          v[8 * i + 2 * j] = __uint_as_float(u << 16);
+          v[8 * i + 2 * j + 1] = __uint_as_float(u & 0xFFFF0000u);
+        }
+      uint32_t out[8];
+      const uint32_t byte = quantize_block32<true>(v, out);
+      aq[s] = valid ? v8i{(int)out[0], (int)out[1], (int)out[2], (int)out[3], 0, 0, 0, 0} : v8i{};
+      lo_b |= byte << (8 * s);
+    } else {
+      uint32_t mlo = max(bf16_absmax8(raw[4 * s]), bf16_absmax8(raw[4 * s + 1]));
+      uint32_t mhi = max(bf16_absmax8(raw[4 * s + 2]), bf16_absmax8(raw[4 * s + 3]));
+      mlo = max(mlo, (uint32_t)__shfl_xor((int)mlo, 16));
+      mhi = max(mhi, (uint32_t)__shfl_xor((int)mhi, 16));
+      const uint32_t blo = scale_byte_from_amax_bits(mlo << 16, kEmaxE4M3);
+      const uint32_t bhi = scale_byte_from_amax_bits(mhi << 16, kEmaxE4M3);
+      uint32_t lo[4], hi[4];
+      e4m3_encode16(raw[4 * s], raw[4 * s + 1], blo, lo);
+      e4m3_encode16(raw[4 * s + 2], raw[4 * s + 3], bhi, hi);
+      aq[s] = valid ? v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                          (int)hi[3]}
+                    : v8i{};
+      lo_b |= blo << (8 * s);
+      hi_b |= bhi << (8 * s);
+    }
+    // one step's temporaries at a time (the compiler would otherwise interleave the
+    // steps and run out of registers)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (kActFP4) {
+    as = valid ? (int)lo_b : 0;
+  } else {
+    const uint32_t got = (uint32_t)__shfl_xor((int)(g == 2 ? lo_b : hi_b), 48);
+    const uint32_t b = g == 0 ? lo_b : g == 3 ? hi_b : got;
+    as = valid ? (int)b : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // weight-streaming kernel (rows per expert <= 16 * MT)
 //
 // K order inside a 512-k super-step: step s, hardware block hb <-> memory block
@@ -78,9 +189,11 @@ constexpr int kStgBytes = 4 * kStgStride;
 
 // NB: consecutive 64-row blocks per workgroup (FC2 / dense only), streamed one after
 // the other by every wave, so that a wave of a short-K GEMM streams NB super-steps
-template <bool kActFP4, int kMode, bool kYBF16, int MT, int NB = 1>
+// kQ: dense only, M <= 16 - a.act holds the bf16 activations [M][K], quantised in registers
+template <bool kActFP4, int kMode, bool kYBF16, int MT, int NB = 1, bool kQ = false>
 __device__ __forceinline__ void stream_body(const GemmArgs& a) {
   static_assert(NB == 1 || kMode != kModeFC1, "FC1 workgroups own one 64-row block");
+  static_assert(!kQ || (kMode == kModeDense && MT == 1 && NB == 1), "in-register quantisation: dense, one fragment");
   constexpr int kFA = kActFP4 ? kFmtFP4 : kFmtFP8;
   // per wave: two fragment staging areas in the loop, then NB x MT x 16 x 64 fp32 partial sums
   constexpr int kWaveBytes = 2 * kStgBytes > NB * MT * 4096 ? 2 * kStgBytes : NB * MT * 4096;
@@ -158,8 +271,9 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
       if (kMode == kModeFC1) src = a.sorted_pair[row0 + lr] / a.topk;
       else src = row0 + lr;
     }
-    ap[mt] = a.act + src * arow_bytes + 16 * g;
-    asp[mt] = a.act_scale + src * srow_bytes;
+    if (kQ) ap[mt] = a.act + 2 * (src * K + (kActFP4 ? 32 : 16) * g);  // bf16 bytes
+    else ap[mt] = a.act + src * arow_bytes + 16 * g;
+    asp[mt] = kQ ? nullptr : a.act_scale + src * srow_bytes;
   }
 
   v4f acc[NB][MT][4];
@@ -184,10 +298,21 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
     // issue every load of the super-step before any wait: activations and scales
     // (few bytes, mostly L2 hits; rows past m read row 0 and are zeroed below),
     // then the 16 weight lines
-    v4i araw[MT][kActFP4 ? 4 : 8], asraw[MT], sraw[4];
+    v4i araw[MT][kQ ? 16 : kActFP4 ? 4 : 8], asraw[MT], sraw[4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      if (kActFP4) {
+      if constexpr (kQ) {
+        // bf16: 2 bytes per k; E2M1 lanes read k 128 s + 32 g + [0, 32), E4M3 lanes
+        // k 128 s + 16 g + [0, 16) and 128 s + 64 + 16 g + [0, 16)
+        const uint8_t* src = ap[mt] + (int64_t)ss * 1024;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            araw[mt][4 * s + j] =
+                *reinterpret_cast<const v4i*>(src + 256 * s + (kActFP4 ? 16 * j : 16 * (j & 1) + 128 * (j >> 1)));
+        continue;
+      } else if (kActFP4) {
         const uint8_t* src = ap[mt] + (int64_t)ss * 256;
 #pragma unroll
         for (int s = 0; s < 4; ++s) araw[mt][s] = *reinterpret_cast<const v4i*>(src + 64 * s);
@@ -222,7 +347,9 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
           raw[f][s] = buf_load16_nt(wr, wv + 128 * (s >> 1), (uint32_t)((ro + 8 * (s & 1)) * wrow_bytes + ss * 256));
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (nb == 0) {
+      if (nb == 0 && kQ) {
+        if constexpr (kQ) quantize_fragment<kActFP4>(araw[0], avalid[0], aq[0], as[0]);
+      } else if (nb == 0) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const v4i z = v4i{0, 0, 0, 0};
@@ -317,6 +444,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) g
 template <bool kActFP4, int kMode, bool kYBF16, int MT>
 __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
   stream_body<kActFP4, kMode, kYBF16, MT>(a);
+}
+
+// dense GEMM with M <= 16 and bf16 activations quantised in registers
+template <bool kActFP4>
+__global__ void __launch_bounds__(256) gemm_stream_q_kernel(GemmArgs a) {
+  stream_body<kActFP4, kModeDense, false, 1, 1, true>(a);
+}
+
+void launch_stream_q_gemm(bool act_fp4, const GemmArgs& a, dim3 grid, hipStream_t stream) {
+  if (act_fp4) gemm_stream_q_kernel<true><<<grid, 256, 0, stream>>>(a);
+  else gemm_stream_q_kernel<false><<<grid, 256, 0, stream>>>(a);
 }
 
 // decode FC2 (K = I, a few super-steps): two 64-row blocks per workgroup, measured

@@ -39,6 +39,15 @@ int launch_dense_gemm(const uint8_t* qa, const uint8_t* qa_scale, bool act_fp4, 
                       int64_t K, const uint8_t* w, const uint8_t* w_scale, float* c, float* partials,
                       hipStream_t stream);
 
+// dense GEMMs of at most kDenseQRows rows take the bf16 activations straight into the
+// weight-streaming kernel, which quantises them in registers (the codes never leave the
+// compute unit): one launch when dense_q_ksplit is 1, else K slices of dense_ksplit
+// and their fixed-order sum, needing dense_q_ksplit * M * N fp32 of partial sums
+constexpr int64_t kDenseQRows = 16;
+int dense_q_ksplit(int64_t M, int64_t N, int64_t K);
+int launch_dense_q_gemm(const uint16_t* a, bool act_fp4, int64_t M, int64_t N, int64_t K, const uint8_t* w,
+                        const uint8_t* w_scale, float* c, float* partials, hipStream_t stream);
+
 // FP4 weights x bf16 activations (gemm_w4a16.hip): K slices of 4 super-steps for narrow N
 // (w4a16_ksplit > 1 needs w4a16_ksplit * min(M, 64) * N fp32 of partial sums)
 int w4a16_ksplit(int64_t M, int64_t N, int64_t K);

@@ -68,21 +68,32 @@ def test_quantize_errors():
 
 def test_gemm_errors():
     lib = _lib()
-    need = lib.mxfp4_gemm_workspace_bytes(16, 32, 4096, 0)
-    # E4M3 codes + scale bytes + fp32 partial sums of the 2 K slices (8 super-steps of 512)
-    assert need >= 16 * 4096 + 16 * 128 + 2 * 16 * 32 * 4
-    assert lib.mxfp4_gemm_workspace_bytes(16, 32, 4096, 1) < need
+    need = lib.mxfp4_gemm_workspace_bytes(32, 32, 4096, 0)
+    # 17..64 rows: E4M3 codes + scale bytes + fp32 partial sums of the 2 K slices (8 super-steps of 512)
+    assert need >= 32 * 4096 + 32 * 128 + 2 * 32 * 32 * 4
+    assert lib.mxfp4_gemm_workspace_bytes(32, 32, 4096, 1) < need
     # no K split above 64 rows, nor when K fits one slice of 4 super-steps
     assert lib.mxfp4_gemm_workspace_bytes(100, 32, 4096, 0) < 100 * 4096 + 100 * 128 + 512
-    assert lib.mxfp4_gemm_workspace_bytes(16, 32, 2048, 0) < 16 * 2048 + 16 * 64 + 512
+    assert lib.mxfp4_gemm_workspace_bytes(32, 32, 2048, 0) < 32 * 2048 + 32 * 64 + 512
     assert lib.mxfp4_gemm_workspace_bytes(0, 32, 4096, 0) == 0
-    assert lib.mxfp4_gemm(A, 16, 32, 4096 + 64, 0, A, A, A, A, need, None) == SHAPE  # K % 512
-    assert lib.mxfp4_gemm(A, 16, 40, 4096, 0, A, A, A, A, need, None) == SHAPE       # N % 16
-    assert lib.mxfp4_gemm(A, 16, 32, 4096, 2, A, A, A, A, need, None) == FORMAT
-    assert lib.mxfp4_gemm(A, 16, 32, 4096, 0, None, A, A, A, need, None) == NULL
-    assert lib.mxfp4_gemm(A, 16, 32, 4096, 0, A, A, A, A, need - 1, None) == WORKSPACE
-    assert lib.mxfp4_gemm(A, 16, 32, 4096, 0, A, A, A, None, need, None) == WORKSPACE
-    assert lib.mxfp4_gemm(A, 16, 32, 4096, 0, A, U, A, A, need, None) == ALIGN
+    # at most 16 rows: quantised in registers, so no codes; a weight matrix of at most
+    # 1 MiB of codes runs in one launch (no workspace), a larger one in 4-super-step
+    # K slices (fp32 partial sums only)
+    assert lib.mxfp4_gemm_workspace_bytes(16, 32, 4096, 0) == 0
+    assert lib.mxfp4_gemm_workspace_bytes(1, 512, 4096, 1) == 0
+    assert lib.mxfp4_gemm_workspace_bytes(16, 4096, 7168, 0) == 4 * 16 * 4096 * 4
+    assert lib.mxfp4_gemm_workspace_bytes(5, 4096, 7168, 1) == (4 * 5 * 4096 * 4 + 255) // 256 * 256
+    assert lib.mxfp4_gemm(A, 32, 32, 4096 + 64, 0, A, A, A, A, need, None) == SHAPE  # K % 512
+    assert lib.mxfp4_gemm(A, 32, 40, 4096, 0, A, A, A, A, need, None) == SHAPE       # N % 16
+    assert lib.mxfp4_gemm(A, 32, 32, 4096, 2, A, A, A, A, need, None) == FORMAT
+    assert lib.mxfp4_gemm(A, 32, 32, 4096, 0, None, A, A, A, need, None) == NULL
+    assert lib.mxfp4_gemm(A, 32, 32, 4096, 0, A, A, A, A, need - 1, None) == WORKSPACE
+    assert lib.mxfp4_gemm(A, 32, 32, 4096, 0, A, A, A, None, need, None) == WORKSPACE
+    assert lib.mxfp4_gemm(A, 32, 32, 4096, 0, A, U, A, A, need, None) == ALIGN
+    need16 = lib.mxfp4_gemm_workspace_bytes(16, 4096, 7168, 0)
+    assert lib.mxfp4_gemm(A, 16, 4096, 7168, 0, A, A, A, None, need16, None) == WORKSPACE
+    assert lib.mxfp4_gemm(A, 16, 4096, 7168, 0, A, A, A, A, need16 - 1, None) == WORKSPACE
+    assert lib.mxfp4_gemm(A, 16, 4096, 7168, 0, A, A, A, U, need16, None) == ALIGN
     assert lib.mxfp4_gemm(None, 0, 32, 4096, 0, None, None, None, None, 0, None) == OK
     # M > 64 with N % 256 == 0 runs the tiled kernels: operands below 4 GiB (32-bit offsets)
     assert lib.mxfp4_gemm(A, 1 << 20, 256, 8192, 0, A, A, A, A, 1 << 40, None) == UNSUPPORTED
