@@ -97,16 +97,19 @@ int mxfp4_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t K, int 
  * a silent other path), and the dense shapes of the accuracy table in page "【DeepSeek
  * V4】Triton FP4 优化实战" section 第二步 (16 x 32 x 4096 and 64 x 4096 x 7168).
  *   a        [M][K] bf16 activations, quantised inside the call per 32-block to
- *            act_fmt (E4M3 or E2M1) with the rule above; the quantised copy
- *            lives only in `workspace`
+ *            act_fmt (E4M3 or E2M1) with the rule above. For M <= 16 the GEMM
+ *            kernel quantises them in registers and the codes are never written;
+ *            for larger M the quantised copy lives only in `workspace`
  *   w        [N][K/2] E2M1 codes, w_scale [N][K/32] UE8M0
  *   c        [M][N] fp32 output (fp32 accumulation of exact products)
  *   workspace, workspace_bytes: device scratch of at least
  *            mxfp4_gemm_workspace_bytes(M, N, K, act_fmt) bytes (16-byte
- *            aligned): the quantised activations and, for M <= 64, the fp32
- *            partial sums of the K slices; its contents on entry are ignored and
- *            on exit undefined. The slice sums are added in a fixed order, so
- *            results are bit-identical from run to run.
+ *            aligned; may be NULL when that is 0): the quantised activations
+ *            (M > 16) and the fp32 partial sums of the K slices (M <= 64 with a
+ *            long K; for M <= 16 only when the weight codes exceed 1 MiB - below
+ *            that the call is one launch and needs no workspace); its contents on
+ *            entry are ignored and on exit undefined. The slice sums are added in
+ *            a fixed order, so results are bit-identical from run to run.
  * Requires K % 512 == 0 (one 512-k super-step of scaled-MFMA K steps) and
  * N % 16 == 0; M >= 0 (M == 0 is a no-op). For M > 64 with N % 256 == 0 (the
  * tiled kernels) the quantised activations and the weight codes must each stay
