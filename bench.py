@@ -55,9 +55,9 @@ BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,
 # FETCH_SIZE + 1.0 x WRITE_SIZE, checked on an LDS-DMA GEMM of known bytes; the passes and the
 # calibration are in profiles/moe_layer_hbm_traffic.md). They hold only for the GEMM sources
 # they were measured on (sha-256 over GEMM_SOURCES): on any other source traffic = null.
-TRAFFIC_SRC_SHA256 = "b6b6a097a31c415146c1cd207265ea6ca9c1fd4df813573b734973b1da8a4a17"
-TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8844413760, "moe_decode_t8_fused": 1022553481,
-                 "moe_decode_t8": 1008462349, "moe_prefill_t2048_zipf": 3168333104}
+TRAFFIC_SRC_SHA256 = "18da42be9508cf0f3529004cbf46956509a02311c031f0a40c226da7273da9c3"
+TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8862875034, "moe_decode_t8_fused": 1022510490,
+                 "moe_decode_t8": 1008518758, "moe_prefill_t2048_zipf": 3159298560}
 
 
 GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_stream.hip", "gemm_tile.hip", "gemm_wide.hip", "gemm_f8ring.hip",
