@@ -64,7 +64,7 @@ def test_layer_graph_replays_match_eager(T, H, I, E, k, fmt):
         _assert_same(out, want)
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 32, 4096), (64, 512, 7168), (100, 256, 1024)])
+@pytest.mark.parametrize("M,N,K", [(16, 32, 4096), (9, 2048, 4096), (64, 512, 7168), (100, 256, 1024)])
 def test_dense_graph_replays_match_eager(M, N, K):
     a0, ww, ss = (dg.activations(33, M, K),) + tuple(dg.dense_weights(33, N, K, 122, 130))
     w, s = torch.from_numpy(ww).cuda(), torch.from_numpy(ss).cuda()

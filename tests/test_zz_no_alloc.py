@@ -42,6 +42,8 @@ def _both(M, N, K, fmt, seed):
     ((64, 4096, 7168, "e4m3"), (16, 32, 4096, "e4m3")),   # the two dense workloads, large then small
     ((300, 512, 1536, "e2m1"), (37, 48, 5120, "e2m1")),   # tiles, then K slices through the scratch
     ((129, 96, 512, "e4m3"), (70, 256, 1536, "e4m3")),    # 64-row chunks, then FP8 tiles
+    # at most 16 rows (activations quantised in registers): K-slice partials in the array
+    ((16, 4096, 7168, "e4m3"), (5, 2048, 4096, "e2m1")),
 ])
 def test_noalloc_matches_workspace_entry_point(first, second):
     for i, (M, N, K, fmt) in enumerate((first, second)):
