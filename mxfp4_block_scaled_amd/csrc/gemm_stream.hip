@@ -190,14 +190,18 @@ constexpr int kStgBytes = 4 * kStgStride;
 // NB: consecutive 64-row blocks per workgroup (FC2 / dense only), streamed one after
 // the other by every wave, so that a wave of a short-K GEMM streams NB super-steps
 // kQ: dense only, M <= 16 - a.act holds the bf16 activations [M][K], quantised in registers
-template <bool kActFP4, int kMode, bool kYBF16, int MT, int NB = 1, bool kQ = false>
+// WV: waves per workgroup, splitting the K range between them (4; 8 for the one-launch
+// dense GEMM with in-register quantisation, whose single workgroup then streams one
+// super-step per wave instead of two after one another)
+template <bool kActFP4, int kMode, bool kYBF16, int MT, int NB = 1, bool kQ = false, int WV = 4>
 __device__ __forceinline__ void stream_body(const GemmArgs& a) {
   static_assert(NB == 1 || kMode != kModeFC1, "FC1 workgroups own one 64-row block");
   static_assert(!kQ || (kMode == kModeDense && MT == 1 && NB == 1), "in-register quantisation: dense, one fragment");
+  static_assert(WV == 4 || (kQ && WV == 8), "four waves, or eight for the in-register dense kernel");
   constexpr int kFA = kActFP4 ? kFmtFP4 : kFmtFP8;
   // per wave: two fragment staging areas in the loop, then NB x MT x 16 x 64 fp32 partial sums
   constexpr int kWaveBytes = 2 * kStgBytes > NB * MT * 4096 ? 2 * kStgBytes : NB * MT * 4096;
-  __shared__ v4i lds[4][kWaveBytes / 16];
+  __shared__ v4i lds[WV][kWaveBytes / 16];
   // wave-uniform values made visible as such (readfirstlane), so that the K range, and
   // with it every buffer load's scalar offset, stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -293,7 +297,7 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
     ss_hi = min(nss, ss_lo + a.kchunk);
   }
   const int len = ss_hi - ss_lo;
-  const int ss_begin = ss_lo + wave * len / 4, ss_end = ss_lo + (wave + 1) * len / 4;
+  const int ss_begin = ss_lo + wave * len / WV, ss_end = ss_lo + (wave + 1) * len / WV;
   for (int ss = ss_begin; ss < ss_end; ++ss) {
     // issue every load of the super-step before any wait: activations and scales
     // (few bytes, mostly L2 hits; rows past m read row 0 and are zeroed below),
@@ -346,6 +350,14 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
         for (int s = 0; s < 4; ++s)
           raw[f][s] = buf_load16_nt(wr, wv + 128 * (s >> 1), (uint32_t)((ro + 8 * (s & 1)) * wrow_bytes + ss * 256));
       }
+      if constexpr (kQ) {
+        // the bf16 values count as written here, after every weight load has gone out:
+        // their unpacking (plain arithmetic, free to move) would otherwise be scheduled
+        // first and make the weight loads wait for the activations' round trip
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(araw[0][i]));
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (nb == 0 && kQ) {
         if constexpr (kQ) quantize_fragment<kActFP4>(araw[0], avalid[0], aq[0], as[0]);
@@ -391,7 +403,7 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
   void* const out = kMode == kModeDense && a.kchunk > 0
                         ? static_cast<void*>(static_cast<float*>(a.out) + (int64_t)blockIdx.y * a.M * a.N)
                         : a.out;
-  // reduce the 4 K-slices in a fixed order (deterministic)
+  // reduce the WV K-slices in a fixed order (deterministic)
   // (each wave writes only its own area, which it alone used in the loop)
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -404,7 +416,7 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
           reinterpret_cast<float*>(&lds[wave][0])[((nb * MT + mt) * 16 + f * 4 + v) * 64 + lane] = acc[nb][mt][f][v];
   __syncthreads();
   // one (row block, 16-row fragment) item per wave
-  for (int item = wave; item < NB * MT; item += 4) {
+  for (int item = wave; item < NB * MT; item += WV) {
     const int nb = item / MT, mt = item % MT;
     float tot[4][4];
 #pragma unroll
@@ -414,7 +426,10 @@ __device__ __forceinline__ void stream_body(const GemmArgs& a) {
         const int idx = item * 16 + f * 4 + v;
         const float* r = reinterpret_cast<const float*>(&lds[0][0]) + idx * 64 + lane;
         constexpr int kW = kWaveBytes / 4;  // floats per wave area
-        tot[f][v] = ((r[0] + r[kW]) + r[2 * kW]) + r[3 * kW];
+        float t = r[0];
+#pragma unroll
+        for (int w = 1; w < WV; ++w) t += r[w * kW];
+        tot[f][v] = t;
       }
     if (kMode == kModeFC1) {
       epilogue_fc1<kActFP4>(tot, 16 * mt, m, row0, (int64_t)blockIdx.x * 32, a.I, a.h, a.h_scale);
@@ -447,14 +462,23 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a) {
 }
 
 // dense GEMM with M <= 16 and bf16 activations quantised in registers
-template <bool kActFP4>
-__global__ void __launch_bounds__(256) gemm_stream_q_kernel(GemmArgs a) {
-  stream_body<kActFP4, kModeDense, false, 1, 1, true>(a);
+template <bool kActFP4, int WV>
+__global__ void __launch_bounds__(64 * WV) gemm_stream_q_kernel(GemmArgs a) {
+  stream_body<kActFP4, kModeDense, false, 1, 1, true, WV>(a);
 }
 
 void launch_stream_q_gemm(bool act_fp4, const GemmArgs& a, dim3 grid, hipStream_t stream) {
-  if (act_fp4) gemm_stream_q_kernel<true><<<grid, 256, 0, stream>>>(a);
-  else gemm_stream_q_kernel<false><<<grid, 256, 0, stream>>>(a);
+  // one workgroup row over the whole K (no slices) of at least 8 super-steps: eight
+  // waves; else four (measured: 16 x 32 x 4096 in 9.75 instead of 11.37 us per call, but
+  // 16 x 2048 x 2048, 4 super-steps, in 8.22 instead of 7.39 us)
+  const bool wide = grid.y == 1 && a.kchunk == 0 && a.K / 512 >= 8;
+  if (act_fp4) {
+    if (wide) gemm_stream_q_kernel<true, 8><<<grid, 512, 0, stream>>>(a);
+    else gemm_stream_q_kernel<true, 4><<<grid, 256, 0, stream>>>(a);
+  } else {
+    if (wide) gemm_stream_q_kernel<false, 8><<<grid, 512, 0, stream>>>(a);
+    else gemm_stream_q_kernel<false, 4><<<grid, 256, 0, stream>>>(a);
+  }
 }
 
 // decode FC2 (K = I, a few super-steps): two 64-row blocks per workgroup, measured
