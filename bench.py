@@ -55,7 +55,7 @@ BYTES_PER_EXPERT = 4096 * 3584 + 4096 * 224 + 7168 * 1024 + 7168 * 64  # 23,396,
 # FETCH_SIZE + 1.0 x WRITE_SIZE, checked on an LDS-DMA GEMM of known bytes; the passes and the
 # calibration are in profiles/moe_layer_hbm_traffic.md). They hold only for the GEMM sources
 # they were measured on (sha-256 over GEMM_SOURCES): on any other source traffic = null.
-TRAFFIC_SRC_SHA256 = "31d169d5fb3c25f5223174073493b63897cc951d67e1dd0c309d8c989753e60a"
+TRAFFIC_SRC_SHA256 = "3a7190cdea46bb71ff62cb93561c5f3ff45b76bcf51056a30bc9c9514ae3f104"
 TRAFFIC_BYTES = {"moe_prefill_t16384_fp4": 8861863526, "moe_decode_t8_fused": 1022578995,
                  "moe_decode_t8": 1008449229, "moe_prefill_t2048_zipf": 3164287283}
 

@@ -3,7 +3,9 @@
 // loads, and turned into the 16x16x128 scaled MFMA's lane layout through a small
 // per-wave LDS area; the K range is split over the 4 waves of a workgroup and
 // reduced through LDS in a fixed order. One workgroup = one expert x 64 weight
-// rows (FC1: 32 gate + the 32 matching up rows, so SwiGLU stays local).
+// rows (FC1: 32 gate + the 32 matching up rows, so SwiGLU stays local). A dense
+// variant for at most 16 rows takes bf16 activations and quantises them in registers
+// (gemm_stream_q_kernel: 4 waves, or 8 for a one-launch call of at least 8 super-steps).
 #include "gemm_common.hpp"
 
 namespace mxf {
