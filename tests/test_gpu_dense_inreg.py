@@ -82,10 +82,10 @@ def _adversarial(K, seed):
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
-@pytest.mark.parametrize("M,K,seed", [(16, 512, 1), (9, 1024, 2), (1, 512, 3), (16, 4096, 4)])
+@pytest.mark.parametrize("M,K,seed", [(16, 512, 1), (9, 1024, 2), (1, 512, 3), (16, 4096, 4), (7, 1536, 5)])
 def test_in_register_codes_bit_exact(fmt, M, K, seed):
-    """K = 512 / 1024: one launch (no workspace); K = 4096: a one-hot weight matrix of
-    8 MiB of codes, so two K slices and the fixed-order slice sum."""
+    """K = 512 / 1024 / 1536: one launch of four waves (no workspace); K = 4096: a one-hot
+    weight matrix of 8 MiB of codes, so two K slices and the fixed-order slice sum."""
     _check(_adversarial(K, seed)[:M], fmt)
 
 
@@ -107,3 +107,21 @@ def test_in_register_smallest_scale_bytes(fmt):
     q, qs = oracle.moe.quantize_act(oracle.bf16_bits_to_f64(bits), fmt)
     assert qs.min() == 0 and qs.max() < 127
     _check(bits, fmt, scale_byte=191)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_in_register_eight_waves(fmt):
+    """One launch by eight waves (at least 8 super-steps, at most 1 MiB of weight codes):
+    a one-hot weight row for every 96th k of 24 super-steps (three per wave), so codes
+    from every wave's K range come back bit for bit."""
+    M, N, K = 11, 128, 12288  # 768 KB of weight codes: one launch
+    bits = _adversarial(K, 7)[:M]
+    codes = np.zeros((N, K), np.uint8)
+    cols = np.arange(N) * (K // N)
+    codes[np.arange(N), cols] = 2
+    w, s = oracle.pack_e2m1(codes), np.full((N, K // 32), 127, np.uint8)
+    c = ops.mxfp4_gemm(bf16_dev(bits), torch.from_numpy(w).cuda(), torch.from_numpy(s).cuda(), fmt)
+    torch.cuda.synchronize()
+    q, qs = oracle.moe.quantize_act(oracle.bf16_bits_to_f64(bits), fmt)
+    want = oracle.moe.decode_act(q, qs, fmt)[:, cols]
+    assert np.array_equal(host(c).astype(np.float64), want)

@@ -44,6 +44,9 @@ def test_dense_workloads(name):
     # a three-slot turn and one more), 65 rows (the second row group holds a single row),
     # and 513 rows at K = 2048 (the unrolled 16-stage instance, a 1-row third unit)
     (256, 256, 512, "e4m3"), (65, 512, 1024, "e4m3"), (513, 256, 2048, "e4m3"),
+    # at most 16 rows, quantised in registers, one launch by eight waves: 12 super-steps
+    # (waves take one or two) and 16 super-steps with a 16-row N
+    (3, 48, 6144, "e4m3"), (16, 16, 8192, "e2m1"),
 ])
 def test_dense_ragged_shapes(M, N, K, fmt):
     a = dg.activations(M * 7 + N, M, K, outliers=True)
